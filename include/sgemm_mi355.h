@@ -1,0 +1,148 @@
+/*
+ * sgemm_mi355 -- single-precision matrix multiply for AMD Instinct MI355X
+ * (gfx950, CDNA4), C = A.B on row-major FP32 matrices with FP32 accumulation.
+ *
+ * The operation. Element (i, j) of C is the dot product of row i of A and
+ * column j of B: C[i][j] = sum_{k<K} A[i][k] * B[k][j], one multiply and one
+ * add per term, 2*M*N*K floating-point operations per call (ratcatcher.ru
+ * "Matrix multiplication: naive and tiled", section 1; GPU Parallel Book
+ * ch. 9 "Optimised Matrix Multiplication", section 9.1). Matrices are stored
+ * row by row, element (row, col) at offset row*ld + col (ratcatcher page,
+ * section 1); general M, N, K follow the CUDA Handbook, ch. 17, section 17.3.
+ * The scale factors are fixed: alpha = 1, beta = 0, so C is written, never
+ * read.
+ *
+ * Layout of every call:
+ *   A: M x K, element (i, k) at A[(size_t)i*lda + k], lda >= max(1, K)
+ *   B: K x N, element (k, j) at B[(size_t)k*ldb + j], ldb >= max(1, N)
+ *   C: M x N, element (i, j) at C[(size_t)i*ldc + j], ldc >= max(1, N)
+ *   Columns j in [N, ldc) of C (row padding) are never written; padding of A
+ *   and B is never used in a result.
+ *
+ * Ownership and execution. A, B and C are device pointers owned by the
+ * caller; `stream` is the caller's HIP stream (0 = the default stream). A
+ * call validates its arguments on the host, enqueues one kernel on `stream`
+ * and returns without synchronising; results are visible to work ordered
+ * after it on that stream. The library allocates no memory, keeps no mutable
+ * global state (calls are thread-safe) and never synchronises the device.
+ * A kernel fault surfaces at the caller's next synchronisation.
+ *
+ * Precision. Products and sums are FP32 (CDNA4 FP32 matrix instructions in
+ * the main path, FP32 fused multiply-add in the vector path); nothing is
+ * converted to a narrower type. The summation order differs from a plain
+ * k-ascending loop, so results agree with one to within
+ * |C - C_exact| <= 4*K*2^-23*sum_k |A[i][k]*B[k][j]| per element; inputs whose
+ * partial sums are integers below 2^24 give exact results.
+ *
+ * Errors. Every entry point returns SGEMM_MI355_OK (0) or a negative code.
+ * Argument errors are detected on the host before any HIP call; nothing is
+ * enqueued then. No entry point aborts or throws.
+ */
+#ifndef SGEMM_MI355_H
+#define SGEMM_MI355_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGEMM_MI355_OK 0
+#define SGEMM_MI355_ERR_DIM (-1)      /* M, N or K is negative */
+#define SGEMM_MI355_ERR_LD (-2)       /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
+#define SGEMM_MI355_ERR_NULL (-3)     /* a null pointer for a matrix with elements */
+#define SGEMM_MI355_ERR_ALIAS (-4)    /* C's extent overlaps A's or B's */
+#define SGEMM_MI355_ERR_EXTENT (-5)   /* the tile grid exceeds one launch's limits */
+#define SGEMM_MI355_ERR_LAUNCH (-6)   /* the HIP runtime rejected the launch */
+#define SGEMM_MI355_ERR_CONFIG (-7)   /* unknown kernel configuration id */
+#define SGEMM_MI355_ERR_ALIGN (-8)    /* a pointer is not 4-byte aligned */
+
+/*
+ * Main entry point: C = A.B with the kernel configuration the built-in tile
+ * table picks for (M, N, K) (tile sizes chosen by measurement, as the CUDA
+ * Handbook section 17.3 and GPU Parallel Book section 9.6 prescribe).
+ * Quick returns: M == 0 or N == 0 does nothing and returns 0; K == 0 sets the
+ * M x N block of C to +0 (the empty sum). Any 4-byte-aligned pointers and any
+ * leading dimensions allowed above are accepted.
+ */
+int sgemm_mi355(int M, int N, int K,
+                const float *A, int lda,
+                const float *B, int ldb,
+                float *C, int ldc,
+                hipStream_t stream);
+
+/*
+ * Same contract as sgemm_mi355, computed by the vector-FMA comparison kernel
+ * (LDS-tiled register microtile, in the spirit of the register-tiled kernel of
+ * GPU Parallel Book section 9.5 and the 8x8 microtile of the CUDA Handbook
+ * section 17.3) instead of the matrix-core path.
+ */
+int sgemm_mi355_valu(int M, int N, int K,
+                     const float *A, int lda,
+                     const float *B, int ldb,
+                     float *C, int ldc,
+                     hipStream_t stream);
+
+/*
+ * Same contract, with the kernel configuration forced to `config`
+ * (0 <= config < sgemm_mi355_num_configs()); returns SGEMM_MI355_ERR_CONFIG
+ * for an unknown id. Used to measure every configuration (tile tuning) and to
+ * test each one, not only those the table picks.
+ */
+int sgemm_mi355_with_config(int M, int N, int K,
+                            const float *A, int lda,
+                            const float *B, int ldb,
+                            float *C, int ldc,
+                            hipStream_t stream, int config);
+
+/*
+ * Argument validation alone: returns the code the entry points above would
+ * return for these arguments before touching the GPU (0 if they would run).
+ * Pure host code; makes no HIP call.
+ */
+int sgemm_mi355_validate(int M, int N, int K,
+                         const float *A, int lda,
+                         const float *B, int ldb,
+                         const float *C, int ldc);
+
+/* Configuration id the tile table picks for a problem shape (host only). */
+int sgemm_mi355_select_config(int M, int N, int K);
+
+/* Number of kernel configurations compiled into the library. */
+int sgemm_mi355_num_configs(void);
+
+/*
+ * Static description of configuration `config`: a NUL-terminated string such
+ * as "mfma32_256x256x16_w2x2" (kernel kind, block tile BMxBNxBK, waves), or
+ * NULL for an unknown id. The string is owned by the library.
+ */
+const char *sgemm_mi355_config_name(int config);
+
+/*
+ * Tile geometry of configuration `config`: writes the block tile rows (bm),
+ * columns (bn), K-slab depth (bk) and threads per workgroup (threads) through
+ * the non-null pointers; returns 0 or SGEMM_MI355_ERR_CONFIG.
+ */
+int sgemm_mi355_config_info(int config, int *bm, int *bn, int *bk, int *threads);
+
+/*
+ * Diagnostic: the workgroup -> C-tile map every kernel uses. For workgroup
+ * `bid` of a tiles_m x tiles_n grid of block tiles walked in bands of
+ * `group_m` tile rows, writes the tile row (*tm) and column (*tn). Workgroups
+ * are renumbered so consecutive logical ids share one of the 8 XCDs (and its
+ * L2). The map is a bijection on [0, tiles_m*tiles_n). Returns 0, or
+ * SGEMM_MI355_ERR_DIM for out-of-range arguments. Pure host code.
+ */
+int sgemm_mi355_tile_map(int bid, int tiles_m, int tiles_n, int group_m, int *tm, int *tn);
+
+/* Static message for an error code (never NULL). */
+const char *sgemm_mi355_strerror(int code);
+
+/* Library version string, e.g. "0.1.0". */
+const char *sgemm_mi355_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_MI355_H */

@@ -1,0 +1,150 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+* the library loads and exports every function include/*.h declares;
+* argument validation returns the documented codes before any HIP call;
+* configuration metadata and the tile table are consistent;
+* the workgroup -> tile map is a bijection for many grid shapes.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import re
+
+import pytest
+
+import dense_fp32_matrix_02_amd as sg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(sg.LIB_PATH):
+        from dense_fp32_matrix_02_amd import build
+        build.build()
+    return sg.load()
+
+
+def header_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w \*]*?\b(sgemm_mi355\w*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert "sgemm_mi355" in names and len(names) >= 10
+    lib = sg.load()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def test_error_codes_match_header():
+    text = open(os.path.join(ROOT, "include", "sgemm_mi355.h")).read()
+    codes = dict((k, int(v)) for k, v in re.findall(r"#define SGEMM_MI355_(\w+) \(?(-?\d+)\)?", text))
+    assert codes["OK"] == sg.OK
+    for name in ("DIM", "LD", "NULL", "ALIAS", "EXTENT", "LAUNCH", "CONFIG", "ALIGN"):
+        assert codes["ERR_" + name] == getattr(sg, "ERR_" + name)
+        assert sg.strerror(codes["ERR_" + name]) != sg.strerror(12345)
+    assert sg.strerror(0) == "success"
+
+
+# Fake, never-dereferenced device addresses (validation is pure host code).
+A0, B0, C0 = 0x10000000, 0x20000000, 0x30000000
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, 4, A0, 4, B0, 4, C0, 4), sg.ERR_DIM),
+    ((4, -1, 4, A0, 4, B0, 4, C0, 4), sg.ERR_DIM),
+    ((4, 4, -1, A0, 4, B0, 4, C0, 4), sg.ERR_DIM),
+    ((4, 4, 5, A0, 4, B0, 4, C0, 4), sg.ERR_LD),       # lda < K
+    ((4, 5, 4, A0, 4, B0, 4, C0, 5), sg.ERR_LD),       # ldb < N
+    ((4, 5, 4, A0, 4, B0, 5, C0, 4), sg.ERR_LD),       # ldc < N
+    ((4, 4, 0, A0, 0, B0, 4, C0, 4), sg.ERR_LD),       # lda < max(1, K)
+    ((0, 4, 4, 0, 4, 0, 4, 0, 4), sg.OK),              # M == 0: nothing referenced
+    ((4, 0, 4, 0, 4, 0, 1, 0, 1), sg.OK),              # N == 0
+    ((4, 4, 4, A0, 4, B0, 4, 0, 4), sg.ERR_NULL),
+    ((4, 4, 4, 0, 4, B0, 4, C0, 4), sg.ERR_NULL),
+    ((4, 4, 4, A0, 4, 0, 4, C0, 4), sg.ERR_NULL),
+    ((4, 4, 0, 0, 1, 0, 4, C0, 4), sg.OK),             # K == 0: A and B unused
+    ((4, 4, 4, A0 + 2, 4, B0, 4, C0, 4), sg.ERR_ALIGN),
+    ((4, 4, 4, A0, 4, B0 + 1, 4, C0, 4), sg.ERR_ALIGN),
+    ((4, 4, 4, A0, 4, B0, 4, C0 + 3, 4), sg.ERR_ALIGN),
+    ((4, 4, 4, A0 + 4, 4, B0, 4, C0, 4), sg.OK),       # 4-byte alignment is enough
+    ((4, 4, 4, A0, 4, B0, 4, A0 + 60, 4), sg.ERR_ALIAS),   # C starts inside A
+    ((4, 4, 4, A0, 4, B0, 4, B0 - 60, 4), sg.ERR_ALIAS),   # C ends inside B
+    ((4, 4, 4, A0, 4, B0, 4, A0 + 64, 4), sg.OK),          # C right after A
+    ((4, 4, 4, A0, 5, B0, 4, A0 + 4 * 19, 4), sg.OK),      # A extent = 3*5+4 = 19 floats
+    ((4, 4, 4, A0, 5, B0, 4, A0 + 4 * 18, 4), sg.ERR_ALIAS),
+    ((2 ** 31 - 1, 4, 4, A0, 4, B0, 4, C0, 4), sg.ERR_EXTENT),
+])
+def test_validation_codes(args, code):
+    assert sg.sgemm_mi355_validate(*args) == code
+
+
+@pytest.mark.parametrize("fn", ["sgemm_mi355", "sgemm_mi355_valu"])
+def test_entry_points_reject_before_any_hip_call(fn):
+    f = getattr(sg, fn)
+    assert f(-1, 4, 4, A0, 4, B0, 4, C0, 4, 0) == sg.ERR_DIM
+    assert f(4, 4, 5, A0, 4, B0, 4, C0, 4, 0) == sg.ERR_LD
+    assert f(4, 4, 4, A0, 4, B0, 4, A0 + 8, 4, 0) == sg.ERR_ALIAS
+    assert f(0, 4, 4, 0, 4, 0, 4, 0, 4, 0) == sg.OK   # quick return, nothing enqueued
+
+
+def test_with_config_rejects_unknown_ids():
+    n = sg.sgemm_mi355_num_configs()
+    for bad in (-1, n, n + 7):
+        assert sg.sgemm_mi355_with_config(4, 4, 4, A0, 4, B0, 4, C0, 4, 0, bad) == sg.ERR_CONFIG
+        assert sg.sgemm_mi355_config_name(bad) is None
+        with pytest.raises(sg.SgemmError):
+            sg.sgemm_mi355_config_info(bad)
+
+
+def test_config_metadata():
+    names = sg.config_names()
+    assert len(names) == len(set(names)) >= 4
+    for i, name in enumerate(names):
+        bm, bn, bk, threads = sg.sgemm_mi355_config_info(i)
+        assert f"{bm}x{bn}x{bk}" in name
+        assert threads % 64 == 0 and 64 <= threads <= 1024
+        assert name.startswith(("mfma32_", "valu8x8_"))
+        if name.startswith("valu8x8_"):
+            assert threads == (bm // 8) * (bn // 8)
+    assert sg.sgemm_mi355_version().count(".") == 2
+
+
+def test_selection_picks_matrix_core_configs_for_every_workload():
+    import workloads
+    for w in workloads.WORKLOADS:
+        cid = sg.sgemm_mi355_select_config(w.M, w.N, w.K)
+        assert sg.sgemm_mi355_config_name(cid).startswith("mfma32_")
+    for shape in [(1, 1, 1), (7, 3, 9000), (100000, 16, 64), (16, 100000, 64)]:
+        cid = sg.sgemm_mi355_select_config(*shape)
+        assert 0 <= cid < sg.sgemm_mi355_num_configs()
+    assert sg.sgemm_mi355_select_config(-1, 1, 1) == sg.ERR_DIM
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n,group_m", [
+    (1, 1, 4), (1, 7, 4), (7, 1, 4), (3, 5, 2), (16, 16, 4), (32, 32, 4), (24, 16, 4),
+    (13, 29, 8), (8, 8, 1), (64, 3, 16), (5, 64, 3)])
+def test_tile_map_is_a_bijection(tiles_m, tiles_n, group_m):
+    seen = set()
+    for bid in range(tiles_m * tiles_n):
+        tm, tn = sg.sgemm_mi355_tile_map(bid, tiles_m, tiles_n, group_m)
+        assert 0 <= tm < tiles_m and 0 <= tn < tiles_n
+        seen.add((tm, tn))
+    assert len(seen) == tiles_m * tiles_n
+
+
+def test_tile_map_keeps_concurrent_tiles_on_one_xcd_compact():
+    """On a 32 x 32 tile grid each XCD (workgroups b with b % 8 equal) gets
+    consecutive logical tiles; its first 32 resident tiles span 4 tile rows
+    and 8 tile columns instead of a full row of 32."""
+    for xcd in range(8):
+        tiles = [sg.sgemm_mi355_tile_map(8 * s + xcd, 32, 32, 4) for s in range(32)]
+        assert len({tm for tm, _ in tiles}) == 4
+        assert len({tn for _, tn in tiles}) == 8
