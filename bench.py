@@ -128,6 +128,29 @@ def cpu_baseline(w, seconds: float):
     }
 
 
+def copy_probe(nbytes: int, steps: int):
+    """Plain device copy of a known number of bytes (read nbytes, write nbytes)
+    per launch, timed with events; the HBM counters of this kernel give the
+    scale factor from counter units to bytes."""
+    import torch
+
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        torch.mul(src, 1.0, out=dst)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
+                      "ms_per_copy": round(ms, 4), "GBps_read_plus_write": round(8 * n / ms / 1e6, 1)}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +163,9 @@ def main():
     ap.add_argument("--config", default=None, help="force a kernel configuration by name")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="instead of the GEMM, run `steps` plain device copies of BYTES bytes "
+                         "(reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -154,6 +180,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps)
+        return
     sg.load()
     w = workloads.BY_NAME[args.workload]
     config = sg.config_id(args.config) if args.config else None
