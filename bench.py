@@ -56,7 +56,7 @@ def stored_traffic(workload: str, config_name: str):
     return e.get("hbm_bytes_per_launch")
 
 
-def time_gpu(w, steps: int, warmup: int, kind: str, config):
+def time_gpu(w, steps: int, warmup: int, kind: str, config, warmup_ms: float = 0.0):
     import torch
     import dense_fp32_matrix_02_amd as sg
     import workloads
@@ -76,6 +76,12 @@ def time_gpu(w, steps: int, warmup: int, kind: str, config):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # Optional extra warm-up by time: the engine clock ramps up over the first
+    # tens of milliseconds of load after an idle gap.
+    t_warm = time.perf_counter()
+    while (time.perf_counter() - t_warm) * 1e3 < warmup_ms:
+        step()
+        torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
@@ -155,7 +161,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="square8192")
     ap.add_argument("--also", default="square4096",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
@@ -196,7 +202,7 @@ def main():
     also = []
     for name in [s for s in args.also.split(",") if s and s != w.name]:
         wa = workloads.BY_NAME[name]
-        ra = time_gpu(wa, max(args.steps, 20), args.warmup, args.kind, None if args.kind == "mfma" else None)
+        ra = time_gpu(wa, max(args.steps, 20), args.warmup, args.kind, None, warmup_ms=300.0)
         va = wa.flops / (ra["ms_per_step"] * 1e-3) / 1e9
         also.append({"workload": wa.name, "value": round(va, 1), "unit": "GFLOP/s",
                      "ms_per_step": round(ra["ms_per_step"], 4), "config": ra["config_name"],

@@ -19,11 +19,17 @@ LIB_PATH = os.path.join(HERE, "libsgemm_mi355.so")
 OK = 0
 ERR_DIM, ERR_LD, ERR_NULL, ERR_ALIAS, ERR_EXTENT, ERR_LAUNCH, ERR_CONFIG, ERR_ALIGN = (
     -1, -2, -3, -4, -5, -6, -7, -8)
+ERR_STRIDE, ERR_OP = -9, -10
+OP_N, OP_T = 0, 1
 
 _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int
+_F = ctypes.c_float
+_LL = ctypes.c_longlong
 _GEMM = [_I, _I, _I, _P, _I, _P, _I, _P, _I, _P]
+_GEMM_EX = [_I, _I, _I, _I, _I, _F, _P, _I, _P, _I, _F, _P, _I, _P]
+_GEMM_SB = [_I, _I, _I, _I, _I, _F, _P, _I, _LL, _P, _I, _LL, _F, _P, _I, _LL, _I, _P]
 
 
 class SgemmError(RuntimeError):
@@ -45,7 +51,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sgemm_mi355.argtypes = _GEMM
     lib.sgemm_mi355_valu.argtypes = _GEMM
     lib.sgemm_mi355_with_config.argtypes = _GEMM + [_I]
+    lib.sgemm_mi355_ex.argtypes = _GEMM_EX
+    lib.sgemm_mi355_strided_batched.argtypes = _GEMM_SB
+    lib.sgemm_mi355_strided_batched_with_config.argtypes = _GEMM_SB + [_I]
     lib.sgemm_mi355_validate.argtypes = [_I, _I, _I, _P, _I, _P, _I, _P, _I]
+    lib.sgemm_mi355_validate_ex.argtypes = [_I, _I, _I, _I, _I, _F, _P, _I, _LL, _P, _I, _LL, _F, _P,
+                                            _I, _LL, _I]
+    lib.sgemm_mi355_select_config_ex.argtypes = [_I] * 6
+    lib.sgemm_mi355_config_ops.argtypes = [_I, ctypes.POINTER(_I), ctypes.POINTER(_I)]
     lib.sgemm_mi355_select_config.argtypes = [_I, _I, _I]
     lib.sgemm_mi355_num_configs.argtypes = []
     lib.sgemm_mi355_config_name.argtypes = [_I]
@@ -58,7 +71,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sgemm_mi355_version.restype = ctypes.c_char_p
     for name in ("sgemm_mi355", "sgemm_mi355_valu", "sgemm_mi355_with_config", "sgemm_mi355_validate",
                  "sgemm_mi355_select_config", "sgemm_mi355_num_configs", "sgemm_mi355_config_info",
-                 "sgemm_mi355_tile_map"):
+                 "sgemm_mi355_tile_map", "sgemm_mi355_ex", "sgemm_mi355_strided_batched",
+                 "sgemm_mi355_strided_batched_with_config", "sgemm_mi355_validate_ex",
+                 "sgemm_mi355_select_config_ex", "sgemm_mi355_config_ops"):
         getattr(lib, name).restype = _I
     _lib = lib
     return lib
@@ -76,6 +91,43 @@ def sgemm_mi355_valu(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
 
 def sgemm_mi355_with_config(M, N, K, A, lda, B, ldb, C, ldc, stream, config) -> int:
     return load().sgemm_mi355_with_config(M, N, K, A, lda, B, ldb, C, ldc, stream, config)
+
+
+def sgemm_mi355_ex(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream) -> int:
+    return load().sgemm_mi355_ex(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_mi355_strided_batched(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C,
+                                ldc, strideC, batch, stream) -> int:
+    return load().sgemm_mi355_strided_batched(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb,
+                                              strideB, beta, C, ldc, strideC, batch, stream)
+
+
+def sgemm_mi355_strided_batched_with_config(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb,
+                                            strideB, beta, C, ldc, strideC, batch, stream,
+                                            config) -> int:
+    return load().sgemm_mi355_strided_batched_with_config(
+        opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
+        stream, config)
+
+
+def sgemm_mi355_validate_ex(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                            strideC, batch) -> int:
+    return load().sgemm_mi355_validate_ex(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB,
+                                          beta, C, ldc, strideC, batch)
+
+
+def sgemm_mi355_select_config_ex(opA, opB, M, N, K, batch) -> int:
+    return load().sgemm_mi355_select_config_ex(opA, opB, M, N, K, batch)
+
+
+def sgemm_mi355_config_ops(config):
+    """Return (opA, opB) the configuration was built for, or raise SgemmError."""
+    a, b = _I(), _I()
+    rc = load().sgemm_mi355_config_ops(config, ctypes.byref(a), ctypes.byref(b))
+    if rc != OK:
+        raise SgemmError(rc, "sgemm_mi355_config_ops")
+    return a.value, b.value
 
 
 def sgemm_mi355_validate(M, N, K, A, lda, B, ldb, C, ldc) -> int:
@@ -181,3 +233,70 @@ def matmul(A, B, out=None, *, kind: str = "mfma", config: int | None = None, str
     if rc != OK:
         raise SgemmError(rc, "sgemm_mi355")
     return out
+
+
+def _op_dims(X, op):
+    return (X.shape[1], X.shape[0]) if op else (X.shape[0], X.shape[1])
+
+
+def gemm(A, B, C=None, *, opA: int = OP_N, opB: int = OP_N, alpha: float = 1.0, beta: float = 0.0,
+         config: int | None = None, stream=None):
+    """C = alpha*op(A).op(B) + beta*C for FP32 GPU tensors through the C ABI.
+
+    A, B and C are 2-D row-major tensors (rows may be padded); op = OP_T reads
+    the stored matrix transposed. C is allocated (and beta must be 0) when
+    omitted. ``config`` forces a configuration built for (opA, opB).
+    """
+    import torch
+
+    M, K = _op_dims(A, opA)
+    K2, N = _op_dims(B, opB)
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an input C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if tuple(C.shape) != (M, N):
+        raise ValueError("C must be M x N")
+    for x, n in ((A, "A"), (B, "B"), (C, "C")):
+        if x.dtype != torch.float32 or not x.is_cuda:
+            raise TypeError(f"{n} must be a float32 GPU tensor")
+    s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
+    args = (opA, opB, M, N, K, alpha, A.data_ptr(), _ld(A, "A"), 0, B.data_ptr(), _ld(B, "B"), 0,
+            beta, C.data_ptr(), _ld(C, "C"), 0, 1, s)
+    rc = (sgemm_mi355_strided_batched(*args) if config is None
+          else sgemm_mi355_strided_batched_with_config(*args, config))
+    if rc != OK:
+        raise SgemmError(rc, "sgemm_mi355_strided_batched")
+    return C
+
+
+def gemm_strided_batched(A, B, C=None, *, opA: int = OP_N, opB: int = OP_N, alpha: float = 1.0,
+                         beta: float = 0.0, config: int | None = None, stream=None):
+    """Batched form on 3-D tensors (batch, rows, cols) with contiguous rows.
+
+    The batch stride of each operand is its stride(0); a stride of 0 (an
+    expanded tensor) shares one matrix across the batch.
+    """
+    import torch
+
+    batch = C.shape[0] if C is not None else max(A.shape[0], B.shape[0])
+    M, K = _op_dims(A[0], opA)
+    K2, N = _op_dims(B[0], opB)
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an input C")
+        C = torch.empty((batch, M, N), dtype=torch.float32, device=A.device)
+    s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
+    sa = A.stride(0) if A.shape[0] > 1 else 0
+    sb = B.stride(0) if B.shape[0] > 1 else 0
+    args = (opA, opB, M, N, K, alpha, A.data_ptr(), _ld(A[0], "A"), sa, B.data_ptr(), _ld(B[0], "B"),
+            sb, beta, C.data_ptr(), _ld(C[0], "C"), C.stride(0), batch, s)
+    rc = (sgemm_mi355_strided_batched(*args) if config is None
+          else sgemm_mi355_strided_batched_with_config(*args, config))
+    if rc != OK:
+        raise SgemmError(rc, "sgemm_mi355_strided_batched")
+    return C

@@ -67,13 +67,18 @@ __global__ void __launch_bounds__(Cfg::NT) valu_gemm_kernel(GemmArgs g) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int t = threadIdx.x;
 
+  {
+  const int bb = blockIdx.y;  // batch entry (the host launches at most kMaxGridY per grid)
+  const float* A = g.A + (int64_t)bb * g.strideA;
+  const float* B = g.B + (int64_t)bb * g.strideB;
+  float* C = g.C + (int64_t)bb * g.strideC;
   const int a_c = t % Cfg::A_TPR, a_r = t / Cfg::A_TPR;
   const float* a_src[AP];
 #pragma unroll
   for (int p = 0; p < AP; ++p) {
     int row = m0 + a_r + p * Cfg::A_RPP;
     row = row < M ? row : M - 1;
-    a_src[p] = g.A + (int64_t)row * g.lda + 4 * a_c;
+    a_src[p] = A + (int64_t)row * g.lda + 4 * a_c;
   }
   const int b_c = t % Cfg::B_TPR, b_r = t / Cfg::B_TPR;
   const int bcol = n0 + 4 * b_c;
@@ -81,9 +86,8 @@ __global__ void __launch_bounds__(Cfg::NT) valu_gemm_kernel(GemmArgs g) {
   const float* b_src[BP];
 #pragma unroll
   for (int p = 0; p < BP; ++p)
-    b_src[p] = g.B + (int64_t)(b_r + p * Cfg::B_RPP) * g.ldb + (b_valid > 0 ? bcol : 0);
+    b_src[p] = B + (int64_t)(b_r + p * Cfg::B_RPP) * g.ldb + (b_valid > 0 ? bcol : 0);
   const int64_t b_step = (int64_t)BK * g.ldb;
-
   f32x4 ra[AP], rb[BP];
 
   auto load_slab = [&](int k0, int64_t b_off, bool tail) {
@@ -167,16 +171,26 @@ __global__ void __launch_bounds__(Cfg::NT) valu_gemm_kernel(GemmArgs g) {
     __syncthreads();
   }
 
+  const float alpha = g.alpha, beta = g.beta;
+  const bool plain = (alpha == 1.0f && beta == 0.0f);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = m0 + (i < 4 ? 4 * ty + i : BM / 2 + 4 * ty + (i - 4));
     if (row >= M) continue;
-    float* crow = g.C + (int64_t)row * g.ldc;
+    float* crow = C + (int64_t)row * g.ldc;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int col = n0 + (j < 4 ? 4 * tx + j : BN / 2 + 4 * tx + (j - 4));
-      if (col < N) crow[col] = acc[i][j];
+      if (col < N) {
+        if (plain) {
+          crow[col] = acc[i][j];
+        } else {
+          const float v = alpha * acc[i][j];
+          crow[col] = (beta != 0.0f) ? __builtin_fmaf(beta, crow[col], v) : v;
+        }
+      }
     }
+  }
   }
 }
 
@@ -186,32 +200,40 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
   GemmArgs a = g;
   void* args[] = {&a};
   return hipLaunchKernel(reinterpret_cast<const void*>(&valu_gemm_kernel<Cfg>),
-                         dim3((unsigned)tiles), dim3(Cfg::NT), args, 0, stream);
+                         dim3((unsigned)tiles, (unsigned)g.batch), dim3(Cfg::NT), args, 0, stream);
 }
 
-// C[0..M) x [0..N) = +0: the K == 0 result (the empty sum). A fill kernel
-// rather than a memset so the call stays safe inside captured graphs.
-__global__ void __launch_bounds__(256) zero_fill_kernel(float* C, int M, int N, int64_t ldc) {
-  const int64_t total = (int64_t)M * N;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int64_t i = e / N, j = e - i * N;
-    C[i * ldc + j] = 0.0f;
+// C_b = beta * C_b over the M x N block of every batch entry: the result
+// when K == 0 (the empty sum) or alpha == 0. beta == 0 writes +0 without
+// reading C. A plain kernel rather than a memset so the call stays safe
+// inside captured graphs.
+__global__ void __launch_bounds__(256) scale_c_kernel(GemmArgs g) {
+  const int64_t total = (int64_t)g.M * g.N;
+  {
+  const int bb = blockIdx.y;  // batch entry (the host launches at most kMaxGridY per grid)
+    float* C = g.C + (int64_t)bb * g.strideC;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+      const int64_t i = e / g.N, j = e - i * g.N;
+      float* p = C + i * g.ldc + j;
+      *p = (g.beta != 0.0f) ? g.beta * *p : 0.0f;
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_zero_fill(float* C, int M, int N, int64_t ldc, hipStream_t stream) {
-  const int64_t total = (int64_t)M * N;
+hipError_t launch_scale_c(const GemmArgs& g, hipStream_t stream) {
+  const int64_t total = (int64_t)g.M * g.N;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  void* args[] = {&C, &M, &N, &ldc};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&zero_fill_kernel), dim3((unsigned)blocks),
+  GemmArgs a = g;
+  void* args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scale_c_kernel), dim3((unsigned)blocks, (unsigned)g.batch),
                          dim3(256), args, 0, stream);
 }
 
 #define SGEMM_VALU_CFG(BM, BN, BK, G)                                                  \
-  {"valu8x8_" #BM "x" #BN "x" #BK, KIND_VALU, BM, BN, BK, (BM / 8) * (BN / 8), \
+  {"valu8x8_" #BM "x" #BN "x" #BK, KIND_VALU, BM, BN, BK, (BM / 8) * (BN / 8), 0, 0, \
    &launch_valu<ValuCfg<BM, BN, BK, G>>}
 
 KernelConfig kValuConfigs[] = {

@@ -7,6 +7,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 
 #include "sgemm_internal.h"
@@ -21,6 +22,13 @@ struct ShapeEntry {
 #include "tile_table.inc"
 
 constexpr int kCompute = 256;  // compute units on MI355X
+
+// Block tiles the selection rule considers when the table has no entry,
+// largest first (the fastest measured configuration of each tile size).
+const char* const kRuleTiles[] = {"256x128x16_w4x2", "128x64x16_w2x2", "64x64x64_w2x2",
+                                  "32x32x32_w1x1"};
+const char* const kRuleTilesOps[] = {"256x128x16_w4x2", "128x64x16_w2x2", "64x64x32_w2x2",
+                                     "32x32x32_w1x1"};
 
 int num_configs() { return kNumMfmaConfigs + kNumValuConfigs; }
 
@@ -41,82 +49,147 @@ int64_t tiles_for(const KernelConfig& c, int M, int N) {
   return ((int64_t)M + c.bm - 1) / c.bm * (((int64_t)N + c.bn - 1) / c.bn);
 }
 
-// Largest block tile with at least one workgroup per compute unit; if even
-// the smallest tile under-fills the chip, the smallest tile. Among configs of
-// equal tile area the first listed wins.
-int rule_select(int M, int N, int first, int count) {
-  int best = -1;
-  int64_t best_area = -1;
-  int smallest = first;
-  for (int i = first; i < first + count; ++i) {
+const char* ops_suffix(int opA, int opB) {
+  static const char* const s[2][2] = {{"", "_nt"}, {"_tn", "_tt"}};
+  return s[opA][opB];
+}
+
+// The largest rule tile that still gives at least one workgroup per compute
+// unit (counting batch entries), else the smallest.
+int rule_select(int opA, int opB, int M, int N, int batch) {
+  const char* const* tiles = (opA || opB) ? kRuleTilesOps : kRuleTiles;
+  const int n = 4;
+  const int64_t gy = batch < kMaxGridY ? batch : kMaxGridY;
+  int last = -1;
+  for (int i = 0; i < n; ++i) {
+    char name[64];
+    std::snprintf(name, sizeof(name), "mfma32_%s%s", tiles[i], ops_suffix(opA, opB));
+    const int id = config_id(name);
+    if (id < 0) continue;
+    last = id;
+    if (tiles_for(*config_at(id), M, N) * gy >= kCompute) return id;
+  }
+  return last;
+}
+
+int select_mfma(int opA, int opB, int M, int N, int K, int batch) {
+  if (!opA && !opB && batch == 1)
+    for (const ShapeEntry* e = kShapeTable; e->config; ++e)
+      if (e->M == M && e->N == N && e->K == K) {
+        const int id = config_id(e->config);
+        if (id >= 0) return id;
+      }
+  return rule_select(opA, opB, M, N, batch);
+}
+
+// Vector-kernel configurations: largest tile with one workgroup per CU.
+int select_valu(int M, int N) {
+  int best = -1, smallest = -1;
+  int64_t best_area = -1, small_area = INT64_MAX;
+  for (int i = kNumMfmaConfigs; i < num_configs(); ++i) {
     const KernelConfig* c = config_at(i);
     const int64_t area = (int64_t)c->bm * c->bn;
-    const KernelConfig* s = config_at(smallest);
-    if (area < (int64_t)s->bm * s->bn) smallest = i;
-    if (tiles_for(*c, M, N) >= kCompute && area > best_area) {
-      best = i;
-      best_area = area;
-    }
+    if (area < small_area) { small_area = area; smallest = i; }
+    if (tiles_for(*c, M, N) >= kCompute && area > best_area) { best = i; best_area = area; }
   }
   return best >= 0 ? best : smallest;
 }
 
-int select_mfma(int M, int N, int K) {
-  for (const ShapeEntry* e = kShapeTable; e->config; ++e)
-    if (e->M == M && e->N == N && e->K == K) {
-      const int id = config_id(e->config);
-      if (id >= 0) return id;
-    }
-  return rule_select(M, N, 0, kNumMfmaConfigs);
-}
-
-int select_valu(int M, int N) { return rule_select(M, N, kNumMfmaConfigs, kNumValuConfigs); }
-
-bool overlaps(const void* p, uint64_t pbytes, const void* q, uint64_t qbytes) {
-  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+bool overlaps(const void* p, unsigned __int128 pbytes, const void* q, unsigned __int128 qbytes) {
+  const unsigned __int128 a = (uintptr_t)p, b = (uintptr_t)q;
   return a < b + qbytes && b < a + pbytes;
 }
 
-int validate(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
-             const float* C, int ldc) {
-  if (M < 0 || N < 0 || K < 0) return SGEMM_MI355_ERR_DIM;
-  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+struct Problem {
+  int opA, opB, M, N, K;
+  float alpha;
+  const float* A;
+  int lda;
+  long long strideA;
+  const float* B;
+  int ldb;
+  long long strideB;
+  float beta;
+  const float* C;
+  int ldc;
+  long long strideC;
+  int batch;
+};
+
+int validate(const Problem& p) {
+  if ((p.opA != 0 && p.opA != 1) || (p.opB != 0 && p.opB != 1)) return SGEMM_MI355_ERR_OP;
+  if (p.M < 0 || p.N < 0 || p.K < 0 || p.batch < 0) return SGEMM_MI355_ERR_DIM;
+  // Rows of the stored matrices: A is M x K (opA = N) or K x M (opA = T).
+  const int a_cols = p.opA ? p.M : p.K, a_rows = p.opA ? p.K : p.M;
+  const int b_cols = p.opB ? p.K : p.N, b_rows = p.opB ? p.N : p.K;
+  if (p.lda < (a_cols > 1 ? a_cols : 1) || p.ldb < (b_cols > 1 ? b_cols : 1) ||
+      p.ldc < (p.N > 1 ? p.N : 1))
     return SGEMM_MI355_ERR_LD;
-  if (M == 0 || N == 0) return SGEMM_MI355_OK;
-  if (C == nullptr) return SGEMM_MI355_ERR_NULL;
-  if (K > 0 && (A == nullptr || B == nullptr)) return SGEMM_MI355_ERR_NULL;
-  if (((uintptr_t)C & 3) != 0) return SGEMM_MI355_ERR_ALIGN;
-  if (K > 0 && ((((uintptr_t)A) | ((uintptr_t)B)) & 3) != 0) return SGEMM_MI355_ERR_ALIGN;
-  // Index arithmetic inside the kernels keeps row and column numbers in
-  // 32-bit ints with up to one block tile of headroom.
-  if (M > INT_MAX - 1024 || N > INT_MAX - 1024 || K > INT_MAX - 1024) return SGEMM_MI355_ERR_EXTENT;
-  const uint64_t c_bytes = 4 * ((uint64_t)(M - 1) * (uint64_t)ldc + (uint64_t)N);
-  if (K > 0) {
-    const uint64_t a_bytes = 4 * ((uint64_t)(M - 1) * (uint64_t)lda + (uint64_t)K);
-    const uint64_t b_bytes = 4 * ((uint64_t)(K - 1) * (uint64_t)ldb + (uint64_t)N);
-    if (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes))
+  if (p.strideA < 0 || p.strideB < 0 || p.strideC < 0) return SGEMM_MI355_ERR_STRIDE;
+  const unsigned __int128 c_elems =
+      (p.M > 0 && p.N > 0) ? (unsigned __int128)(p.M - 1) * (unsigned)p.ldc + (unsigned)p.N : 0;
+  if (p.batch > 1 && (unsigned __int128)p.strideC < c_elems) return SGEMM_MI355_ERR_STRIDE;
+  if (p.M == 0 || p.N == 0 || p.batch == 0) return SGEMM_MI355_OK;
+  const bool uses_ab = p.alpha != 0.0f && p.K > 0;
+  if (p.C == nullptr) return SGEMM_MI355_ERR_NULL;
+  if (uses_ab && (p.A == nullptr || p.B == nullptr)) return SGEMM_MI355_ERR_NULL;
+  if (((uintptr_t)p.C & 3) != 0) return SGEMM_MI355_ERR_ALIGN;
+  if (uses_ab && ((((uintptr_t)p.A) | ((uintptr_t)p.B)) & 3) != 0) return SGEMM_MI355_ERR_ALIGN;
+  // Row and column numbers stay 32-bit ints inside the kernels with one
+  // block tile of headroom; byte extents must fit the address space.
+  if (p.M > INT_MAX - 1024 || p.N > INT_MAX - 1024 || p.K > INT_MAX - 1024)
+    return SGEMM_MI355_ERR_EXTENT;
+  const unsigned __int128 nb = (unsigned __int128)(p.batch - 1);
+  const unsigned __int128 c_bytes = 4 * (nb * (unsigned long long)p.strideC + c_elems);
+  const unsigned __int128 limit = (unsigned __int128)1 << 62;
+  if (c_bytes > limit) return SGEMM_MI355_ERR_EXTENT;
+  if (uses_ab) {
+    const unsigned __int128 a_elems = (unsigned __int128)(a_rows - 1) * (unsigned)p.lda + (unsigned)a_cols;
+    const unsigned __int128 b_elems = (unsigned __int128)(b_rows - 1) * (unsigned)p.ldb + (unsigned)b_cols;
+    const unsigned __int128 a_bytes = 4 * (nb * (unsigned long long)p.strideA + a_elems);
+    const unsigned __int128 b_bytes = 4 * (nb * (unsigned long long)p.strideB + b_elems);
+    if (a_bytes > limit || b_bytes > limit) return SGEMM_MI355_ERR_EXTENT;
+    if (overlaps(p.C, c_bytes, p.A, a_bytes) || overlaps(p.C, c_bytes, p.B, b_bytes))
       return SGEMM_MI355_ERR_ALIAS;
   }
   return SGEMM_MI355_OK;
 }
 
-int run(int M, int N, int K, const float* A, int lda, const float* B, int ldb, float* C,
-        int ldc, hipStream_t stream, int config) {
-  const int v = validate(M, N, K, A, lda, B, ldb, C, ldc);
+int run(const Problem& p, float* C, hipStream_t stream, int config) {
+  const int v = validate(p);
   if (v != SGEMM_MI355_OK) return v;
   const KernelConfig* cfg = config_at(config);
-  if (cfg == nullptr) return SGEMM_MI355_ERR_CONFIG;
-  if (M == 0 || N == 0) return SGEMM_MI355_OK;
-  hipError_t err;
-  if (K == 0) {
-    err = launch_zero_fill(C, M, N, ldc, stream);
-  } else {
-    const int64_t tiles = tiles_for(*cfg, M, N);
-    if (tiles * cfg->threads > (int64_t)UINT32_MAX) return SGEMM_MI355_ERR_EXTENT;
-    const GemmArgs g{M, N, K, A, lda, B, ldb, C, ldc};
-    err = cfg->launch(g, stream);
+  if (cfg == nullptr || cfg->transA != p.opA || cfg->transB != p.opB) return SGEMM_MI355_ERR_CONFIG;
+  if (p.M == 0 || p.N == 0 || p.batch == 0) return SGEMM_MI355_OK;
+  const GemmArgs g{p.M,     p.N,       p.K,       p.A,       p.lda,     p.B,      p.ldb,
+                   C,       p.ldc,     p.alpha,   p.beta,    p.strideA, p.strideB, p.strideC,
+                   p.batch};
+  const bool scale_only = (p.K == 0 || p.alpha == 0.0f);
+  if (!scale_only && tiles_for(*cfg, p.M, p.N) * cfg->threads > (int64_t)UINT32_MAX)
+    return SGEMM_MI355_ERR_EXTENT;
+  // One launch per kMaxGridY batch entries (grid.y indexes the entry).
+  for (int b0 = 0; b0 < p.batch; b0 += kMaxGridY) {
+    GemmArgs gc = g;
+    gc.batch = (p.batch - b0) < kMaxGridY ? (p.batch - b0) : kMaxGridY;
+    gc.C = C + (int64_t)b0 * p.strideC;
+    if (!scale_only) {
+      gc.A = p.A + (int64_t)b0 * p.strideA;
+      gc.B = p.B + (int64_t)b0 * p.strideB;
+    }
+    const hipError_t err = scale_only ? launch_scale_c(gc, stream) : cfg->launch(gc, stream);
+    if (err != hipSuccess) return SGEMM_MI355_ERR_LAUNCH;
   }
-  return err == hipSuccess ? SGEMM_MI355_OK : SGEMM_MI355_ERR_LAUNCH;
+  return SGEMM_MI355_OK;
+}
+
+Problem plain(int M, int N, int K, const float* A, int lda, const float* B, int ldb, const float* C,
+              int ldc) {
+  return Problem{0, 0, M, N, K, 1.0f, A, lda, 0, B, ldb, 0, 0.0f, C, ldc, 0, 1};
+}
+
+int select_for(const Problem& p) {
+  if (p.opA < 0 || p.opA > 1 || p.opB < 0 || p.opB > 1) return 0;
+  return select_mfma(p.opA, p.opB, p.M < 0 ? 0 : p.M, p.N < 0 ? 0 : p.N, p.K, p.batch < 1 ? 1 : p.batch);
 }
 
 }  // namespace
@@ -128,29 +201,65 @@ extern "C" {
 
 int sgemm_mi355(int M, int N, int K, const float* A, int lda, const float* B, int ldb, float* C,
                 int ldc, hipStream_t stream) {
-  if (M < 0 || N < 0 || K < 0) return SGEMM_MI355_ERR_DIM;
-  return run(M, N, K, A, lda, B, ldb, C, ldc, stream, select_mfma(M, N, K));
+  const Problem p = plain(M, N, K, A, lda, B, ldb, C, ldc);
+  return run(p, C, stream, select_for(p));
 }
 
 int sgemm_mi355_valu(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
                      float* C, int ldc, hipStream_t stream) {
-  if (M < 0 || N < 0 || K < 0) return SGEMM_MI355_ERR_DIM;
-  return run(M, N, K, A, lda, B, ldb, C, ldc, stream, select_valu(M, N));
+  const Problem p = plain(M, N, K, A, lda, B, ldb, C, ldc);
+  return run(p, C, stream, select_valu(M < 0 ? 0 : M, N < 0 ? 0 : N));
 }
 
 int sgemm_mi355_with_config(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
                             float* C, int ldc, hipStream_t stream, int config) {
-  return run(M, N, K, A, lda, B, ldb, C, ldc, stream, config);
+  return run(plain(M, N, K, A, lda, B, ldb, C, ldc), C, stream, config);
+}
+
+int sgemm_mi355_ex(int opA, int opB, int M, int N, int K, float alpha, const float* A, int lda,
+                   const float* B, int ldb, float beta, float* C, int ldc, hipStream_t stream) {
+  const Problem p{opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1};
+  return run(p, C, stream, select_for(p));
+}
+
+int sgemm_mi355_strided_batched(int opA, int opB, int M, int N, int K, float alpha,
+                                const float* A, int lda, long long strideA, const float* B, int ldb,
+                                long long strideB, float beta, float* C, int ldc,
+                                long long strideC, int batch, hipStream_t stream) {
+  const Problem p{opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch};
+  return run(p, C, stream, select_for(p));
+}
+
+int sgemm_mi355_strided_batched_with_config(int opA, int opB, int M, int N, int K, float alpha,
+                                            const float* A, int lda, long long strideA,
+                                            const float* B, int ldb, long long strideB, float beta,
+                                            float* C, int ldc, long long strideC, int batch,
+                                            hipStream_t stream, int config) {
+  const Problem p{opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch};
+  return run(p, C, stream, config);
 }
 
 int sgemm_mi355_validate(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
                          const float* C, int ldc) {
-  return validate(M, N, K, A, lda, B, ldb, C, ldc);
+  return validate(plain(M, N, K, A, lda, B, ldb, C, ldc));
+}
+
+int sgemm_mi355_validate_ex(int opA, int opB, int M, int N, int K, float alpha, const float* A,
+                            int lda, long long strideA, const float* B, int ldb, long long strideB,
+                            float beta, const float* C, int ldc, long long strideC, int batch) {
+  return validate(Problem{opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
+                          strideC, batch});
 }
 
 int sgemm_mi355_select_config(int M, int N, int K) {
   if (M < 0 || N < 0 || K < 0) return SGEMM_MI355_ERR_DIM;
-  return select_mfma(M, N, K);
+  return select_mfma(0, 0, M, N, K, 1);
+}
+
+int sgemm_mi355_select_config_ex(int opA, int opB, int M, int N, int K, int batch) {
+  if ((opA != 0 && opA != 1) || (opB != 0 && opB != 1)) return SGEMM_MI355_ERR_OP;
+  if (M < 0 || N < 0 || K < 0 || batch < 0) return SGEMM_MI355_ERR_DIM;
+  return select_mfma(opA, opB, M, N, K, batch < 1 ? 1 : batch);
 }
 
 int sgemm_mi355_num_configs(void) { return num_configs(); }
@@ -170,6 +279,14 @@ int sgemm_mi355_config_info(int config, int* bm, int* bn, int* bk, int* threads)
   return SGEMM_MI355_OK;
 }
 
+int sgemm_mi355_config_ops(int config, int* opA, int* opB) {
+  const KernelConfig* c = config_at(config);
+  if (!c) return SGEMM_MI355_ERR_CONFIG;
+  if (opA) *opA = c->transA;
+  if (opB) *opB = c->transB;
+  return SGEMM_MI355_OK;
+}
+
 int sgemm_mi355_tile_map(int bid, int tiles_m, int tiles_n, int group_m, int* tm, int* tn) {
   if (tiles_m <= 0 || tiles_n <= 0 || group_m <= 0 || bid < 0 ||
       (int64_t)tiles_m * tiles_n > INT_MAX || bid >= tiles_m * tiles_n || !tm || !tn)
@@ -181,18 +298,20 @@ int sgemm_mi355_tile_map(int bid, int tiles_m, int tiles_n, int group_m, int* tm
 const char* sgemm_mi355_strerror(int code) {
   switch (code) {
     case SGEMM_MI355_OK: return "success";
-    case SGEMM_MI355_ERR_DIM: return "a matrix dimension is negative";
+    case SGEMM_MI355_ERR_DIM: return "a matrix dimension or the batch count is negative";
     case SGEMM_MI355_ERR_LD: return "a leading dimension is smaller than its row length";
     case SGEMM_MI355_ERR_NULL: return "null pointer for a matrix with elements";
     case SGEMM_MI355_ERR_ALIAS: return "C overlaps A or B";
     case SGEMM_MI355_ERR_EXTENT: return "problem too large for one launch";
     case SGEMM_MI355_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
-    case SGEMM_MI355_ERR_CONFIG: return "unknown kernel configuration id";
+    case SGEMM_MI355_ERR_CONFIG: return "unknown kernel configuration, or one built for other operand layouts";
     case SGEMM_MI355_ERR_ALIGN: return "a matrix pointer is not 4-byte aligned";
+    case SGEMM_MI355_ERR_STRIDE: return "a batch stride is negative, or batch entries of C overlap";
+    case SGEMM_MI355_ERR_OP: return "an operand op is neither SGEMM_MI355_OP_N nor SGEMM_MI355_OP_T";
     default: return "unknown error code";
   }
 }
 
-const char* sgemm_mi355_version(void) { return "0.1.0"; }
+const char* sgemm_mi355_version(void) { return "0.2.0"; }
 
 }  // extern "C"

@@ -6,8 +6,13 @@
 
 namespace sgemm_impl {
 
-// Arguments of one C = A.B call, passed to the kernels by value. Leading
-// dimensions are 64-bit so every offset row*ld + col is computed in 64 bits.
+// Arguments of one launch, passed to the kernels by value. The operation is
+//   C_b = alpha * op(A_b) . op(B_b) + beta * C_b,   b = 0 .. batch-1,
+// with X_b = X + b * strideX. op(A) is M x K: A itself (row-major M x K,
+// element (i, k) at A[i*lda + k]) or, with transA, the transpose of a
+// row-major K x M matrix (element (i, k) at A[k*lda + i]); likewise op(B) is
+// K x N from a K x N matrix or, with transB, from an N x K matrix. When
+// beta == 0, C is not read. Offsets are computed in 64 bits.
 struct GemmArgs {
   int M, N, K;
   const float* A;
@@ -16,6 +21,9 @@ struct GemmArgs {
   int64_t ldb;
   float* C;
   int64_t ldc;
+  float alpha, beta;
+  int64_t strideA, strideB, strideC;
+  int batch;
 };
 
 using LaunchFn = hipError_t (*)(const GemmArgs&, hipStream_t);
@@ -27,18 +35,25 @@ struct KernelConfig {
   int kind;
   int bm, bn, bk;
   int threads;
+  int transA, transB;  // operand layouts the kernel reads
   LaunchFn launch;
 };
 
-// Defined in kernels_mfma.hip and kernels_valu.hip.
-extern KernelConfig kMfmaConfigs[];  // host-only tables (not const: a const
-                                      // global would also be emitted on the device)
+// Host-only tables (not const: a const global would also be emitted for the
+// device). Defined in kernels_mfma.hip and kernels_valu.hip.
+extern KernelConfig kMfmaConfigs[];
 extern const int kNumMfmaConfigs;
 extern KernelConfig kValuConfigs[];
 extern const int kNumValuConfigs;
 
-// C[0..M) x [0..N) = +0 (the K == 0 case). Defined in kernels_valu.hip.
-hipError_t launch_zero_fill(float* C, int M, int N, int64_t ldc, hipStream_t s);
+// C_b = beta * C_b over the M x N block of every batch entry of the launch
+// (the K == 0 or alpha == 0 case); beta == 0 writes +0 without reading C.
+// Defined in kernels_valu.hip.
+hipError_t launch_scale_c(const GemmArgs& g, hipStream_t s);
+
+// Batch entries per launch: each launch covers one batch entry per grid.y
+// index, and larger batches are split into several launches on the host.
+constexpr int kMaxGridY = 65535;
 
 // Workgroup -> C-tile map shared by all kernels. Workgroups are dispatched
 // round-robin over the 8 XCDs (workgroup b runs on XCD b % 8), each XCD with
@@ -47,7 +62,7 @@ hipError_t launch_zero_fill(float* C, int M, int N, int64_t ldc, hipStream_t s);
 // tile rows, column by column, so the tiles resident on one XCD at a time
 // share a few A row panels and B column panels in that XCD's L2.
 __host__ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int group_m,
-                                            int& tm, int& tn) {
+                                                     int& tm, int& tn) {
   const int nwg = tiles_m * tiles_n;
   const int q = nwg >> 3, rem = nwg & 7;
   const int xcd = bid & 7, slot = bid >> 3;

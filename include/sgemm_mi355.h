@@ -56,6 +56,12 @@ extern "C" {
 #define SGEMM_MI355_ERR_LAUNCH (-6)   /* the HIP runtime rejected the launch */
 #define SGEMM_MI355_ERR_CONFIG (-7)   /* unknown kernel configuration id */
 #define SGEMM_MI355_ERR_ALIGN (-8)    /* a pointer is not 4-byte aligned */
+#define SGEMM_MI355_ERR_STRIDE (-9)   /* a batch stride is negative, or batch entries of C overlap */
+#define SGEMM_MI355_ERR_OP (-10)      /* an op argument is neither OP_N nor OP_T */
+
+/* Operand ops for the general entry points (row-major storage throughout). */
+#define SGEMM_MI355_OP_N 0 /* op(X) = X */
+#define SGEMM_MI355_OP_T 1 /* op(X) = X^T */
 
 /*
  * Main entry point: C = A.B with the kernel configuration the built-in tile
@@ -96,6 +102,54 @@ int sgemm_mi355_with_config(int M, int N, int K,
                             hipStream_t stream, int config);
 
 /*
+ * General product, the BLAS form of the same operation:
+ *   C = alpha * op(A) . op(B) + beta * C,
+ * op(A) M x K and op(B) K x N, all matrices row-major:
+ *   opA = OP_N: A is M x K, element (i, k) at A[i*lda + k], lda >= max(1, K);
+ *   opA = OP_T: A is K x M, op(A)(i, k) = A[k*lda + i],     lda >= max(1, M);
+ *   opB = OP_N: B is K x N, element (k, j) at B[k*ldb + j], ldb >= max(1, N);
+ *   opB = OP_T: B is N x K, op(B)(k, j) = B[j*ldb + k],     ldb >= max(1, K).
+ * The product is the dot-product definition of the pages (see above); the
+ * scale factors extend it the way the BLAS interface does. When beta == 0, C
+ * is not read (NaN in C does not propagate). When alpha == 0 or K == 0, A and
+ * B are not read and C = beta * C. The product is rounded to FP32, scaled by
+ * alpha, and then beta * C is added with one fused multiply-add.
+ * Errors as above, plus SGEMM_MI355_ERR_OP for an op other than OP_N/OP_T.
+ */
+int sgemm_mi355_ex(int opA, int opB, int M, int N, int K, float alpha,
+                   const float *A, int lda, const float *B, int ldb,
+                   float beta, float *C, int ldc, hipStream_t stream);
+
+/*
+ * Strided batch of independent general products in one launch:
+ *   C_b = alpha * op(A_b) . op(B_b) + beta * C_b,  b = 0 .. batch-1,
+ * with A_b = A + b*strideA, B_b = B + b*strideB, C_b = C + b*strideC
+ * (strides in elements). strideA or strideB may be 0 (one operand shared by
+ * every product); strides are never negative, and when batch > 1 strideC
+ * must keep the C_b apart (strideC >= (M-1)*ldc + N), else
+ * SGEMM_MI355_ERR_STRIDE. batch == 0 does nothing; a negative batch is
+ * SGEMM_MI355_ERR_DIM. C may not overlap any A_b or B_b. The batch is a second
+ * grid dimension, so many small products fill the chip together.
+ */
+int sgemm_mi355_strided_batched(int opA, int opB, int M, int N, int K, float alpha,
+                                const float *A, int lda, long long strideA,
+                                const float *B, int ldb, long long strideB,
+                                float beta, float *C, int ldc, long long strideC,
+                                int batch, hipStream_t stream);
+
+/*
+ * sgemm_mi355_strided_batched with the kernel configuration forced to
+ * `config`, which must have been built for this (opA, opB) pair
+ * (sgemm_mi355_config_ops), else SGEMM_MI355_ERR_CONFIG. For tuning and
+ * tests.
+ */
+int sgemm_mi355_strided_batched_with_config(int opA, int opB, int M, int N, int K, float alpha,
+                                            const float *A, int lda, long long strideA,
+                                            const float *B, int ldb, long long strideB,
+                                            float beta, float *C, int ldc, long long strideC,
+                                            int batch, hipStream_t stream, int config);
+
+/*
  * Argument validation alone: returns the code the entry points above would
  * return for these arguments before touching the GPU (0 if they would run).
  * Pure host code; makes no HIP call.
@@ -105,8 +159,26 @@ int sgemm_mi355_validate(int M, int N, int K,
                          const float *B, int ldb,
                          const float *C, int ldc);
 
+/*
+ * Validation of the general/batched arguments alone (pure host code, no HIP
+ * call): the code sgemm_mi355_strided_batched would return before launching.
+ */
+int sgemm_mi355_validate_ex(int opA, int opB, int M, int N, int K, float alpha,
+                            const float *A, int lda, long long strideA,
+                            const float *B, int ldb, long long strideB,
+                            float beta, const float *C, int ldc, long long strideC, int batch);
+
 /* Configuration id the tile table picks for a problem shape (host only). */
 int sgemm_mi355_select_config(int M, int N, int K);
+
+/* Configuration id chosen for a general/batched problem (host only). */
+int sgemm_mi355_select_config_ex(int opA, int opB, int M, int N, int K, int batch);
+
+/*
+ * Operand ops a configuration was built for: writes OP_N/OP_T through the
+ * non-null pointers; returns 0 or SGEMM_MI355_ERR_CONFIG.
+ */
+int sgemm_mi355_config_ops(int config, int *opA, int *opB);
 
 /* Number of kernel configurations compiled into the library. */
 int sgemm_mi355_num_configs(void);
@@ -138,7 +210,7 @@ int sgemm_mi355_tile_map(int bid, int tiles_m, int tiles_n, int group_m, int *tm
 /* Static message for an error code (never NULL). */
 const char *sgemm_mi355_strerror(int code);
 
-/* Library version string, e.g. "0.1.0". */
+/* Library version string, e.g. "0.2.0". */
 const char *sgemm_mi355_version(void);
 
 #ifdef __cplusplus

@@ -36,6 +36,11 @@ def load(path: str = _build.LIB) -> ctypes.CDLL:
     lib.ref_sgemm_f32.restype = None
     lib.ref_sgemm_f64_abs.argtypes = [_I, _I, _I, _P, _I, _P, _I, _P, _P]
     lib.ref_sgemm_f64_abs.restype = None
+    lib.ref_sgemm_ex_f32.argtypes = [_I, _I, _I, _I, _I, ctypes.c_float, _P, _I, _P, _I,
+                                     ctypes.c_float, _P, _I]
+    lib.ref_sgemm_ex_f32.restype = None
+    lib.ref_sgemm_ex_f64_abs.argtypes = [_I, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P]
+    lib.ref_sgemm_ex_f64_abs.restype = None
     lib.ref_max_threads.restype = _I
     lib.ref_set_threads.argtypes = [_I]
     _LIBS[path] = lib
@@ -88,6 +93,68 @@ def sgemm_f64_abs(A: np.ndarray, B: np.ndarray, lib: ctypes.CDLL | None = None):
     pb, ldb = _operand(B, "B")
     lib.ref_sgemm_f64_abs(M, N, K, pa, lda, pb, ldb, C64.ctypes.data, S.ctypes.data)
     return C64, S
+
+
+def _op_shape(X: np.ndarray, op: int):
+    """Rows and columns of op(X) for a stored 2-D array X."""
+    return (X.shape[1], X.shape[0]) if op else X.shape
+
+
+def sgemm_ex_f32(opA: int, opB: int, alpha: float, A: np.ndarray, B: np.ndarray, beta: float,
+                 C: np.ndarray, K: int | None = None, lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """C = alpha*op(A).op(B) + beta*C in FP32, in place on C (M x N, rows may
+    be padded). op(X) = X for op 0, X^T for op 1 (row-major storage). With
+    alpha == 0 or K == 0, A and B are not read (they may be empty arrays; pass
+    K explicitly then)."""
+    lib = lib or load()
+    M, N = C.shape
+    if K is None:
+        Ma, K = _op_shape(A, opA)
+        Kb, Nb = _op_shape(B, opB)
+        if (Ma, Kb, Nb) != (M, K, N):
+            raise ValueError("operand shapes do not match C")
+    pa, lda = _operand(A, "A") if A.size else (0, max(1, (M if opA else K)))
+    pb, ldb = _operand(B, "B") if B.size else (0, max(1, (K if opB else N)))
+    pc, ldc = _operand(C, "C")
+    lib.ref_sgemm_ex_f32(opA, opB, M, N, K, float(alpha), pa, lda, pb, ldb, float(beta), pc, ldc)
+    return C
+
+
+def sgemm_ex_f64_abs(opA: int, opB: int, A: np.ndarray, B: np.ndarray,
+                     lib: ctypes.CDLL | None = None):
+    """Return (P64, S): op(A).op(B) accumulated in FP64 and sum_k |a*b|."""
+    lib = lib or load()
+    M, K = _op_shape(A, opA)
+    K2, N = _op_shape(B, opB)
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    P = np.empty((M, N), dtype=np.float64)
+    S = np.empty((M, N), dtype=np.float64)
+    pa, lda = _operand(A, "A")
+    pb, ldb = _operand(B, "B")
+    lib.ref_sgemm_ex_f64_abs(opA, opB, M, N, K, pa, lda, pb, ldb, P.ctypes.data, S.ctypes.data)
+    return P, S
+
+
+def check_ex_against_f64(C: np.ndarray, alpha: float, P64: np.ndarray, S: np.ndarray,
+                         beta: float, C0: np.ndarray, K: int, frob_tol: float = 1e-5):
+    """Acceptance for the general form: with R = alpha*P64 + beta*C0 (FP64),
+    every |C - R| <= |alpha|*4*K*2^-23*S + 2^-22*(|alpha*P64| + |beta*C0|)
+    (the product bound plus one rounding each of the scaling, the beta term
+    and the sum), and ||C - R||_F / ||R||_F <= frob_tol. Returns (ok, worst,
+    rel)."""
+    C = np.asarray(C, dtype=np.float64)
+    bterm = beta * np.asarray(C0, dtype=np.float64) if beta != 0.0 else 0.0
+    R = alpha * P64 + bterm
+    bound = abs(alpha) * elementwise_bound(K, S) + 2.0 ** -22 * (np.abs(alpha * P64) + np.abs(bterm))
+    err = np.abs(C - R)
+    finite = np.isfinite(C).all()
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / bound, np.where(err > 0, np.inf, 0.0))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    denom = float(np.linalg.norm(R))
+    rel = float(np.linalg.norm(C - R)) / denom if denom > 0 else float(np.linalg.norm(C))
+    return bool(finite and worst <= 1.0 and rel <= frob_tol), worst, rel
 
 
 def max_threads(lib: ctypes.CDLL | None = None) -> int:

@@ -35,6 +35,14 @@
  * C64 is the "FP64-accumulated reference" for error bounds; S scales the
  * per-element bound |C - C64| <= c*K*2^-23*S.
  *
+ * ref_sgemm_ex_f32 / ref_sgemm_ex_f64_abs: the general form
+ * C = alpha*op(A).op(B) + beta*C with op(X) = X or X^T on row-major storage
+ * (the BLAS interface around the same product). The pages define only the
+ * product; the reading taken for the rest: the product t is the FP32 sum
+ * above, then C = fl(fl(alpha*t) + fl(beta*c)), each operation rounded
+ * separately; C is not read when beta == 0 (the beta term is absent), and A
+ * and B are not read when alpha == 0 or K == 0 (the alpha term is absent).
+ *
  * Pinned by tests/test_oracle_cpu.py against brute force in exact rational
  * arithmetic, identity and all-ones closed forms, the transpose identity,
  * K = 1 products, exact small-integer results and a BLAS FP64 product.
@@ -114,6 +122,75 @@ void ref_sgemm_f64_abs(int M, int N, int K,
                 c[j] = c[j] + p;
                 s[j] = s[j] + fabs(p);
             }
+        }
+    }
+}
+
+/* op(A)(i, k) and op(B)(k, j) on row-major storage. */
+static inline float op_a(int opA, const float *A, int lda, int i, int k)
+{
+    return opA ? A[(size_t)k * (size_t)lda + i] : A[(size_t)i * (size_t)lda + k];
+}
+
+static inline float op_b(int opB, const float *B, int ldb, int k, int j)
+{
+    return opB ? B[(size_t)j * (size_t)ldb + k] : B[(size_t)k * (size_t)ldb + j];
+}
+
+/* C = alpha*op(A).op(B) + beta*C in FP32; the product term is the FP32 sum
+ * from +0 with k ascending, then fl(fl(alpha*t) + fl(beta*c)). */
+void ref_sgemm_ex_f32(int opA, int opB, int M, int N, int K, float alpha,
+                      const float *A, int lda, const float *B, int ldb,
+                      float beta, float *C, int ldc)
+{
+    if (M <= 0 || N <= 0) return;
+    const int use_ab = (alpha != 0.0f) && K > 0;
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < M; ++i) {
+        float *c = C + (size_t)i * (size_t)ldc;
+        for (int j = 0; j < N; ++j) {
+            float t = 0.0f;
+            if (use_ab) {
+                for (int k = 0; k < K; ++k) {
+                    float p = op_a(opA, A, lda, i, k) * op_b(opB, B, ldb, k, j);
+                    t = t + p;
+                }
+            }
+            float out;
+            if (use_ab && beta != 0.0f) {
+                float at = alpha * t;
+                float bc = beta * c[j];
+                out = at + bc;
+            } else if (use_ab) {
+                out = alpha * t;
+            } else if (beta != 0.0f) {
+                out = beta * c[j];
+            } else {
+                out = 0.0f;
+            }
+            c[j] = out;
+        }
+    }
+}
+
+/* P64 = op(A).op(B) and S = sum_k |op(A)(i,k)*op(B)(k,j)| in FP64, dense
+ * M x N (row stride N), k ascending. */
+void ref_sgemm_ex_f64_abs(int opA, int opB, int M, int N, int K,
+                          const float *A, int lda, const float *B, int ldb,
+                          double *P64, double *S)
+{
+    if (M <= 0 || N <= 0) return;
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < M; ++i) {
+        for (int j = 0; j < N; ++j) {
+            double t = 0.0, s = 0.0;
+            for (int k = 0; k < K; ++k) {
+                double p = (double)op_a(opA, A, lda, i, k) * (double)op_b(opB, B, ldb, k, j);
+                t = t + p;
+                s = s + fabs(p);
+            }
+            P64[(size_t)i * (size_t)N + j] = t;
+            S[(size_t)i * (size_t)N + j] = s;
         }
     }
 }

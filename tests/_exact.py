@@ -73,3 +73,34 @@ def sequential_f32(A: np.ndarray, B: np.ndarray):
                 s = round_to_f32(s + round_to_f32(Af[i][k] * Bf[k][j]))
             out[i][j] = s
     return out
+
+
+def sequential_f32_ex(opA: int, opB: int, alpha: float, A: np.ndarray, B: np.ndarray,
+                      beta: float, C: np.ndarray):
+    """General form, exactly rounded: t = FP32 sum (k ascending, product and
+    add rounded separately), then fl(fl(alpha*t) + fl(beta*c)); the beta term
+    is absent when beta == 0 and the alpha term when alpha == 0 or K == 0."""
+    opa = A.T if opA else A
+    opb = B.T if opB else B
+    M, K = opa.shape
+    N = opb.shape[1]
+    al, be = Fraction(float(np.float32(alpha))), Fraction(float(np.float32(beta)))
+    use_ab = al != 0 and K > 0
+    out = [[None] * N for _ in range(M)]
+    for i in range(M):
+        for j in range(N):
+            t = Fraction(0)
+            if use_ab:
+                for k in range(K):
+                    t = round_to_f32(t + round_to_f32(fr(opa[i, k]) * fr(opb[k, j])))
+            c = fr(C[i, j]) if be != 0 else Fraction(0)
+            if use_ab and be != 0:
+                v = round_to_f32(round_to_f32(al * t) + round_to_f32(be * c))
+            elif use_ab:
+                v = round_to_f32(al * t)
+            elif be != 0:
+                v = round_to_f32(be * c)
+            else:
+                v = Fraction(0)
+            out[i][j] = v
+    return out

@@ -47,7 +47,7 @@ def test_error_codes_match_header():
     text = open(os.path.join(ROOT, "include", "sgemm_mi355.h")).read()
     codes = dict((k, int(v)) for k, v in re.findall(r"#define SGEMM_MI355_(\w+) \(?(-?\d+)\)?", text))
     assert codes["OK"] == sg.OK
-    for name in ("DIM", "LD", "NULL", "ALIAS", "EXTENT", "LAUNCH", "CONFIG", "ALIGN"):
+    for name in ("DIM", "LD", "NULL", "ALIAS", "EXTENT", "LAUNCH", "CONFIG", "ALIGN", "STRIDE", "OP"):
         assert codes["ERR_" + name] == getattr(sg, "ERR_" + name)
         assert sg.strerror(codes["ERR_" + name]) != sg.strerror(12345)
     assert sg.strerror(0) == "success"
@@ -148,3 +148,81 @@ def test_tile_map_keeps_concurrent_tiles_on_one_xcd_compact():
         tiles = [sg.sgemm_mi355_tile_map(8 * s + xcd, 32, 32, 4) for s in range(32)]
         assert len({tm for tm, _ in tiles}) == 4
         assert len({tn for _, tn in tiles}) == 8
+
+
+# ---- general form and strided batch: validation only (no kernel runs) -------
+
+def vex(opA=0, opB=0, M=4, N=4, K=4, alpha=1.0, A=A0, lda=None, sA=0, B=B0, ldb=None, sB=0,
+        beta=0.0, C=C0, ldc=None, sC=0, batch=1):
+    lda = lda if lda is not None else max(1, M if opA else K)
+    ldb = ldb if ldb is not None else max(1, K if opB else N)
+    ldc = ldc if ldc is not None else max(1, N)
+    return sg.sgemm_mi355_validate_ex(opA, opB, M, N, K, alpha, A, lda, sA, B, ldb, sB, beta, C, ldc,
+                                      sC, batch)
+
+
+def test_validate_ex_ops_and_leading_dims():
+    assert vex() == sg.OK
+    assert vex(opA=2) == sg.ERR_OP and vex(opB=-1) == sg.ERR_OP
+    # opA = T: A is K x M, so lda >= M; opB = T: B is N x K, so ldb >= K
+    assert vex(opA=1, M=9, K=3, lda=9) == sg.OK
+    assert vex(opA=1, M=9, K=3, lda=8) == sg.ERR_LD
+    assert vex(opA=0, M=9, K=3, lda=3) == sg.OK
+    assert vex(opB=1, N=7, K=5, ldb=5) == sg.OK
+    assert vex(opB=1, N=7, K=5, ldb=4) == sg.ERR_LD
+    assert vex(opB=0, N=7, K=5, ldb=6) == sg.ERR_LD
+
+
+def test_validate_ex_batch_and_strides():
+    assert vex(batch=-1) == sg.ERR_DIM
+    assert vex(batch=0, A=0, B=0, C=0) == sg.OK            # nothing to do
+    assert vex(sA=-1) == sg.ERR_STRIDE
+    assert vex(batch=3, sC=15) == sg.ERR_STRIDE            # C_b overlap: extent is 16
+    assert vex(batch=3, sC=16, sA=0, sB=0, B=B0 + 10 ** 6) == sg.OK   # shared A and B
+    assert vex(batch=1, sC=0) == sg.OK
+    # C's batched range [C0, C0 + 4*(2*100 + 16)) reaches into a B placed after it
+    assert vex(batch=3, sC=100, B=C0 + 4 * 200) == sg.ERR_ALIAS
+    assert vex(batch=3, sC=100, B=C0 + 4 * 216) == sg.OK
+
+
+def test_validate_ex_alpha_zero_and_k_zero_skip_a_and_b():
+    assert vex(alpha=0.0, A=0, B=0, beta=2.0) == sg.OK
+    assert vex(K=0, lda=1, A=0, B=0, beta=0.5) == sg.OK
+    assert vex(alpha=1.0, A=0) == sg.ERR_NULL
+    assert vex(alpha=0.0, A=0, B=0, C=0) == sg.ERR_NULL
+
+
+def test_general_entry_points_reject_before_any_hip_call():
+    assert sg.sgemm_mi355_ex(3, 0, 4, 4, 4, 1.0, A0, 4, B0, 4, 0.0, C0, 4, 0) == sg.ERR_OP
+    assert sg.sgemm_mi355_strided_batched(0, 0, 4, 4, 4, 1.0, A0, 4, 0, B0, 4, 0, 0.0, C0, 4, 1, 2, 0) \
+        == sg.ERR_STRIDE
+    assert sg.sgemm_mi355_strided_batched(0, 0, 4, 4, 4, 1.0, A0, 4, 0, B0, 4, 0, 0.0, C0, 4, 16, 0, 0) \
+        == sg.OK
+
+
+def test_config_ops_and_config_op_mismatch():
+    n = sg.sgemm_mi355_num_configs()
+    seen = set()
+    for cid in range(n):
+        ops = sg.sgemm_mi355_config_ops(cid)
+        seen.add(ops)
+        name = sg.sgemm_mi355_config_name(cid)
+        suffix = {(0, 0): "", (1, 0): "_tn", (0, 1): "_nt", (1, 1): "_tt"}[ops]
+        assert name.endswith(suffix) if suffix else not name.endswith(("_tn", "_nt", "_tt"))
+        other = (1 - ops[0], ops[1])
+        assert sg.sgemm_mi355_strided_batched_with_config(other[0], other[1], 4, 4, 4, 1.0, A0, 4, 0, B0, 4, 0,
+                                                          0.0, C0, 4, 0, 1, 0, cid) == sg.ERR_CONFIG
+    assert seen == {(0, 0), (0, 1), (1, 0), (1, 1)}
+
+
+def test_select_config_ex_matches_ops():
+    for opA, opB in [(0, 0), (0, 1), (1, 0), (1, 1)]:
+        for shape in [(1, 1, 1, 1), (4096, 4096, 4096, 1), (64, 64, 64, 1000), (3001, 2047, 1537, 3)]:
+            cid = sg.sgemm_mi355_select_config_ex(opA, opB, *shape)
+            assert sg.sgemm_mi355_config_ops(cid) == (opA, opB)
+    assert sg.sgemm_mi355_select_config_ex(2, 0, 1, 1, 1, 1) == sg.ERR_OP
+    assert sg.sgemm_mi355_select_config_ex(0, 0, 1, 1, 1, -1) == sg.ERR_DIM
+    # many small products: the batch fills the chip, so a large tile is fine
+    big = sg.sgemm_mi355_select_config_ex(0, 0, 256, 256, 256, 64)
+    small = sg.sgemm_mi355_select_config_ex(0, 0, 256, 256, 256, 1)
+    assert sg.sgemm_mi355_config_info(big)[0] >= sg.sgemm_mi355_config_info(small)[0]

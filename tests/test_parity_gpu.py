@@ -78,6 +78,21 @@ def _edge_sizes(tile):
     return sorted({1, 2, 3, tile - 1, tile, tile + 1, 2 * tile + 3})
 
 
+def _stored(X, op):
+    """The array to pass for op(X) = X (op 0) or X^T (op 1)."""
+    return X.t().contiguous() if op else X
+
+
+def _run_config(A, B, cid):
+    """C = A.B through the configuration `cid`, with A and B stored in the
+    layout the configuration reads (transposed copies for its T operands)."""
+    opA, opB = sg.sgemm_mi355_config_ops(cid)
+    print(f"[gpu] config={CONFIG_NAMES[cid]} M={A.shape[0]} N={B.shape[1]} K={A.shape[1]}", flush=True)
+    C = sg.gemm(G.dev(_stored(A, opA)), G.dev(_stored(B, opB)), opA=opA, opB=opB, config=cid)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
 @pytest.mark.parametrize("cid", CONFIG_IDS, ids=CONFIG_NAMES)
 def test_every_config_edges_exact(cid):
     """Every compiled configuration, forced, on M, N around its block tile and
@@ -91,14 +106,14 @@ def test_every_config_edges_exact(cid):
             for K in (Ks if (M in (1, bm + 1) or N in (1, bn + 1)) else Ks[::3]):
                 seed += 1
                 A, B = workloads.draw(M, N, K, seed, "int4")
-                C = G.gemm(A, B, config=cid)
+                C = _run_config(A, B, cid)
                 G.check_exact(C, np_(A), np_(B))
 
 
 @pytest.mark.parametrize("cid", CONFIG_IDS, ids=CONFIG_NAMES)
 def test_every_config_float_ragged(cid):
     A, B = workloads.draw(301, 257, 203, 77, "normal")
-    C = G.gemm(A, B, config=cid)
+    C = _run_config(A, B, cid)
     G.check_float(C, np_(A), np_(B))
 
 
