@@ -21,11 +21,13 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# MI355X published peaks (dense): FP32 matrix 157.3 TFLOP/s; FP32 vector
-# 157.3 TFLOP/s with packed FP32, 78.6 TFLOP/s with scalar FMA (256 CU x 4
-# SIMD x 16 lanes x 2 FLOP x 2.4 GHz); HBM3E 8 TB/s.
+# MI355X published peaks (dense): FP32 matrix 157.3 TFLOP/s (256 CU x 2.4 GHz
+# x 256 FLOP/clk/CU); FP32 vector 157.3 TFLOP/s, which plain VOP2 v_fmac_f32
+# with VGPR operands reaches on gfx950 (a throughput probe measured 143
+# TFLOP/s; VOP3 v_fma_f32 with two scalar operands runs at half that rate);
+# HBM3E 8 TB/s.
 PEAK_MFMA_TFLOPS = 157.3
-PEAK_VALU_TFLOPS = 78.6
+PEAK_VECTOR_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
@@ -227,8 +229,8 @@ def main():
                    "ldc": w.ldc, "dist": w.dist, "seed": w.seed, "kernel": r["config_name"],
                    "kind": args.kind},
         "frac_fp32_mfma_peak": round(value / (PEAK_MFMA_TFLOPS * 1e3), 4),
-        "frac_fp32_vector_peak": {"packed_157.3": round(value / (PEAK_MFMA_TFLOPS * 1e3), 4),
-                                  "scalar_78.6": round(value / (PEAK_VALU_TFLOPS * 1e3), 4)},
+        "frac_fp32_vector_peak": round(value / (PEAK_VECTOR_TFLOPS * 1e3), 4),
+        "peaks_tflops": {"fp32_mfma": PEAK_MFMA_TFLOPS, "fp32_vector": PEAK_VECTOR_TFLOPS},
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),

@@ -190,11 +190,19 @@ def config_id(name: str) -> int:
 # ---- torch convenience wrapper (marshalling only) ---------------------------
 
 def _ld(x, name):
+    """Leading dimension (row stride in elements) of a 2-D tensor whose rows
+    are contiguous. A dimension of size 1 may carry any stride in torch, so
+    its stride is not looked at."""
     if x.dim() != 2:
         raise ValueError(f"{name} must be 2-D")
-    if x.shape[0] and x.shape[1] and x.stride(1) != 1:
+    rows, cols = x.shape
+    if rows and cols > 1 and x.stride(1) != 1:
         raise ValueError(f"{name} rows must be contiguous (stride(1) == 1)")
-    return max(x.stride(0) if x.shape[0] > 1 else x.shape[1], 1)
+    if rows > 1:
+        if x.stride(0) < cols:
+            raise ValueError(f"{name} row stride is smaller than its row length")
+        return max(x.stride(0), 1)
+    return max(cols, 1)
 
 
 def matmul(A, B, out=None, *, kind: str = "mfma", config: int | None = None, stream=None):

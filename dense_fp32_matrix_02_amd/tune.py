@@ -82,7 +82,8 @@ def main(argv=None):
 
     names = sg.config_names()
     kinds = args.kinds.split(",")
-    cands = [i for i, n in enumerate(names) if n.startswith(tuple(kinds))]
+    cands = [i for i, n in enumerate(names)
+             if n.startswith(tuple(kinds)) and sg.sgemm_mi355_config_ops(i) == (0, 0)]
     results = []
     for (M, N, K) in parse_shapes(args.shapes):
         A, B = workloads.draw(M, N, K, 1234, "uniform")

@@ -226,3 +226,18 @@ def test_select_config_ex_matches_ops():
     big = sg.sgemm_mi355_select_config_ex(0, 0, 256, 256, 256, 64)
     small = sg.sgemm_mi355_select_config_ex(0, 0, 256, 256, 256, 1)
     assert sg.sgemm_mi355_config_info(big)[0] >= sg.sgemm_mi355_config_info(small)[0]
+
+
+def test_binding_leading_dimension_of_torch_tensors():
+    """Row stride read from torch tensors: padded rows keep their stride, and
+    a size-1 dimension's stride (arbitrary in torch) is ignored."""
+    import torch
+    from dense_fp32_matrix_02_amd._binding import _ld
+    assert _ld(torch.zeros(1, 2).t().contiguous(), "x") == 1      # (2, 1) with strides (1, 2)
+    assert _ld(torch.zeros(3, 1), "x") == 1
+    assert _ld(torch.zeros(1, 5), "x") == 5
+    assert _ld(torch.zeros(4, 8)[:, :5], "x") == 8
+    with pytest.raises(ValueError):
+        _ld(torch.zeros(4, 8).t(), "x")
+    with pytest.raises(ValueError):
+        _ld(torch.zeros(2, 3, 4), "x")
