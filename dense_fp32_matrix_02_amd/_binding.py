@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libsgemm_mi355.so")
 OK = 0
 ERR_DIM, ERR_LD, ERR_NULL, ERR_ALIAS, ERR_EXTENT, ERR_LAUNCH, ERR_CONFIG, ERR_ALIGN = (
     -1, -2, -3, -4, -5, -6, -7, -8)
-ERR_STRIDE, ERR_OP = -9, -10
+ERR_STRIDE, ERR_OP, ERR_WORKSPACE = -9, -10, -11
 OP_N, OP_T = 0, 1
 
 _lib = None
@@ -54,6 +54,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sgemm_mi355_ex.argtypes = _GEMM_EX
     lib.sgemm_mi355_strided_batched.argtypes = _GEMM_SB
     lib.sgemm_mi355_strided_batched_with_config.argtypes = _GEMM_SB + [_I]
+    lib.sgemm_mi355_splitk.argtypes = _GEMM_EX[:-1] + [_I, _P, ctypes.c_size_t, _P]
+    lib.sgemm_mi355_splitk_with_config.argtypes = _GEMM_EX[:-1] + [_I, _P, ctypes.c_size_t, _P, _I]
+    lib.sgemm_mi355_splitk_workspace_size.argtypes = [_I, _I, _I, _I]
+    lib.sgemm_mi355_splitk_workspace_size.restype = ctypes.c_size_t
+    lib.sgemm_mi355_select_splitk.argtypes = [_I, _I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]
     lib.sgemm_mi355_validate.argtypes = [_I, _I, _I, _P, _I, _P, _I, _P, _I]
     lib.sgemm_mi355_validate_ex.argtypes = [_I, _I, _I, _I, _I, _F, _P, _I, _LL, _P, _I, _LL, _F, _P,
                                             _I, _LL, _I]
@@ -73,7 +78,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                  "sgemm_mi355_select_config", "sgemm_mi355_num_configs", "sgemm_mi355_config_info",
                  "sgemm_mi355_tile_map", "sgemm_mi355_ex", "sgemm_mi355_strided_batched",
                  "sgemm_mi355_strided_batched_with_config", "sgemm_mi355_validate_ex",
-                 "sgemm_mi355_select_config_ex", "sgemm_mi355_config_ops"):
+                 "sgemm_mi355_select_config_ex", "sgemm_mi355_config_ops", "sgemm_mi355_splitk",
+                 "sgemm_mi355_splitk_with_config", "sgemm_mi355_select_splitk"):
         getattr(lib, name).restype = _I
     _lib = lib
     return lib
@@ -109,6 +115,31 @@ def sgemm_mi355_strided_batched_with_config(opA, opB, M, N, K, alpha, A, lda, st
     return load().sgemm_mi355_strided_batched_with_config(
         opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch,
         stream, config)
+
+
+def sgemm_mi355_splitk(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, splits, workspace,
+                       workspace_bytes, stream) -> int:
+    return load().sgemm_mi355_splitk(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, splits,
+                                     workspace, workspace_bytes, stream)
+
+
+def sgemm_mi355_splitk_with_config(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, splits,
+                                   workspace, workspace_bytes, stream, config) -> int:
+    return load().sgemm_mi355_splitk_with_config(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                                 splits, workspace, workspace_bytes, stream, config)
+
+
+def sgemm_mi355_splitk_workspace_size(M, N, K, splits) -> int:
+    return load().sgemm_mi355_splitk_workspace_size(M, N, K, splits)
+
+
+def sgemm_mi355_select_splitk(opA, opB, M, N, K):
+    """Return (splits, config) the library suggests, or raise SgemmError."""
+    sp, cf = _I(), _I()
+    rc = load().sgemm_mi355_select_splitk(opA, opB, M, N, K, ctypes.byref(sp), ctypes.byref(cf))
+    if rc != OK:
+        raise SgemmError(rc, "sgemm_mi355_select_splitk")
+    return sp.value, cf.value
 
 
 def sgemm_mi355_validate_ex(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
@@ -307,4 +338,38 @@ def gemm_strided_batched(A, B, C=None, *, opA: int = OP_N, opB: int = OP_N, alph
           else sgemm_mi355_strided_batched_with_config(*args, config))
     if rc != OK:
         raise SgemmError(rc, "sgemm_mi355_strided_batched")
+    return C
+
+
+def gemm_splitk(A, B, C=None, *, splits: int | None = None, opA: int = OP_N, opB: int = OP_N,
+                alpha: float = 1.0, beta: float = 0.0, workspace=None, config: int | None = None,
+                stream=None):
+    """Split-K product C = alpha*op(A).op(B) + beta*C through the C ABI.
+
+    ``splits`` defaults to the library's suggestion; the workspace (a float32
+    GPU tensor of at least sgemm_mi355_splitk_workspace_size bytes) is
+    allocated with torch when omitted. Returns C.
+    """
+    import torch
+
+    M, K = _op_dims(A, opA)
+    K2, N = _op_dims(B, opB)
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an input C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if splits is None:
+        splits, suggested = sgemm_mi355_select_splitk(opA, opB, M, N, K)
+        config = suggested if config is None else config
+    need = sgemm_mi355_splitk_workspace_size(M, N, K, splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 4) + 3) // 4, dtype=torch.float32, device=A.device)
+    s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
+    args = (opA, opB, M, N, K, alpha, A.data_ptr(), _ld(A, "A"), B.data_ptr(), _ld(B, "B"), beta,
+            C.data_ptr(), _ld(C, "C"), splits, workspace.data_ptr(), workspace.numel() * 4, s)
+    rc = (sgemm_mi355_splitk(*args) if config is None else sgemm_mi355_splitk_with_config(*args, config))
+    if rc != OK:
+        raise SgemmError(rc, "sgemm_mi355_splitk")
     return C

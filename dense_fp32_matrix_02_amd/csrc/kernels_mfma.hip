@@ -196,7 +196,8 @@ __global__ void __launch_bounds__(Cfg::NT) mfma_gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float As[2 * OpA::FLOATS];
   __shared__ __attribute__((aligned(16))) float Bs[2 * OpB::FLOATS];
 
-  const int M = g.M, N = g.N, K = g.K;
+  const int M = g.M, N = g.N;
+  const int K = (blockIdx.y == gridDim.y - 1) ? g.k_last : g.K;  // last split-K chunk may be short
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, Cfg::GROUP_M, tm, tn);

@@ -155,6 +155,26 @@ int validate(const Problem& p) {
   return SGEMM_MI355_OK;
 }
 
+// Launch `cfg` (or the C = beta*C kernel) over all batch entries of g, one
+// launch per kMaxGridY entries; the last entry of the whole batch has
+// K = g.k_last.
+hipError_t launch_batches(const KernelConfig* cfg, const GemmArgs& g, bool scale_only,
+                          hipStream_t stream) {
+  for (int b0 = 0; b0 < g.batch; b0 += kMaxGridY) {
+    GemmArgs gc = g;
+    gc.batch = (g.batch - b0) < kMaxGridY ? (g.batch - b0) : kMaxGridY;
+    gc.C = g.C + (int64_t)b0 * g.strideC;
+    gc.k_last = (b0 + gc.batch == g.batch) ? g.k_last : g.K;
+    if (!scale_only) {
+      gc.A = g.A + (int64_t)b0 * g.strideA;
+      gc.B = g.B + (int64_t)b0 * g.strideB;
+    }
+    const hipError_t err = scale_only ? launch_scale_c(gc, stream) : cfg->launch(gc, stream);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
 int run(const Problem& p, float* C, hipStream_t stream, int config) {
   const int v = validate(p);
   if (v != SGEMM_MI355_OK) return v;
@@ -163,23 +183,104 @@ int run(const Problem& p, float* C, hipStream_t stream, int config) {
   if (p.M == 0 || p.N == 0 || p.batch == 0) return SGEMM_MI355_OK;
   const GemmArgs g{p.M,     p.N,       p.K,       p.A,       p.lda,     p.B,      p.ldb,
                    C,       p.ldc,     p.alpha,   p.beta,    p.strideA, p.strideB, p.strideC,
-                   p.batch};
+                   p.batch, p.K};
   const bool scale_only = (p.K == 0 || p.alpha == 0.0f);
   if (!scale_only && tiles_for(*cfg, p.M, p.N) * cfg->threads > (int64_t)UINT32_MAX)
     return SGEMM_MI355_ERR_EXTENT;
-  // One launch per kMaxGridY batch entries (grid.y indexes the entry).
-  for (int b0 = 0; b0 < p.batch; b0 += kMaxGridY) {
-    GemmArgs gc = g;
-    gc.batch = (p.batch - b0) < kMaxGridY ? (p.batch - b0) : kMaxGridY;
-    gc.C = C + (int64_t)b0 * p.strideC;
-    if (!scale_only) {
-      gc.A = p.A + (int64_t)b0 * p.strideA;
-      gc.B = p.B + (int64_t)b0 * p.strideB;
-    }
-    const hipError_t err = scale_only ? launch_scale_c(gc, stream) : cfg->launch(gc, stream);
-    if (err != hipSuccess) return SGEMM_MI355_ERR_LAUNCH;
-  }
+  return launch_batches(cfg, g, scale_only, stream) == hipSuccess ? SGEMM_MI355_OK
+                                                                  : SGEMM_MI355_ERR_LAUNCH;
+}
+
+// ---- split-K -----------------------------------------------------------------
+// K is cut into `splits` chunks of kchunk values (a multiple of 32; the last
+// chunk takes the rest). Chunk s multiplies op(A)[:, s*kchunk ...] by
+// op(B)[s*kchunk ..., :] into the dense M x N partial W_s of the caller's
+// workspace (one strided-batched launch, batch entry = chunk), then one
+// reduction kernel forms C = alpha * (W_0 + W_1 + ...) + beta * C, adding the
+// partials in ascending order so repeated calls give identical bits.
+
+constexpr int kMaxSplits = 256;
+
+struct SplitPlan {
+  int splits;  // effective number of chunks (<= requested)
+  int kchunk;
+  int k_last;
+};
+
+SplitPlan plan_splits(int K, int splits) {
+  if (splits < 1) splits = 1;
+  if (K <= 0) return SplitPlan{1, K, K};
+  int64_t kc = ((int64_t)K + splits - 1) / splits;
+  kc = (kc + 31) / 32 * 32;
+  const int eff = (int)(((int64_t)K + kc - 1) / kc);
+  if (eff <= 1) return SplitPlan{1, K, K};
+  return SplitPlan{eff, (int)kc, (int)(K - (int64_t)(eff - 1) * kc)};
+}
+
+uint64_t splitk_bytes(int M, int N, int splits) {
+  return (M > 0 && N > 0 && splits > 1) ? 4ull * (uint64_t)splits * (uint64_t)M * (uint64_t)N : 0;
+}
+
+int run_splitk(const Problem& p, float* C, int splits, float* W, size_t w_bytes, hipStream_t stream,
+               int config) {
+  if (splits < 1 || splits > kMaxSplits) return SGEMM_MI355_ERR_DIM;
+  const int v = validate(p);
+  if (v != SGEMM_MI355_OK) return v;
+  const SplitPlan sp = plan_splits(p.K, splits);
+  const bool uses_ab = p.alpha != 0.0f && p.K > 0 && p.M > 0 && p.N > 0;
+  if (!uses_ab || sp.splits == 1) return run(p, C, stream, config);
+  const KernelConfig* cfg = config_at(config);
+  if (cfg == nullptr || cfg->transA != p.opA || cfg->transB != p.opB) return SGEMM_MI355_ERR_CONFIG;
+  const uint64_t need = splitk_bytes(p.M, p.N, sp.splits);
+  if (W == nullptr) return SGEMM_MI355_ERR_NULL;
+  if (((uintptr_t)W & 3) != 0) return SGEMM_MI355_ERR_ALIGN;
+  if ((uint64_t)w_bytes < need) return SGEMM_MI355_ERR_WORKSPACE;
+  // The workspace may not overlap A, B or C.
+  const unsigned __int128 a_bytes =
+      4 * ((unsigned __int128)((p.opA ? p.K : p.M) - 1) * (unsigned)p.lda + (unsigned)(p.opA ? p.M : p.K));
+  const unsigned __int128 b_bytes =
+      4 * ((unsigned __int128)((p.opB ? p.N : p.K) - 1) * (unsigned)p.ldb + (unsigned)(p.opB ? p.K : p.N));
+  const unsigned __int128 c_bytes = 4 * ((unsigned __int128)(p.M - 1) * (unsigned)p.ldc + (unsigned)p.N);
+  if (overlaps(W, need, p.A, a_bytes) || overlaps(W, need, p.B, b_bytes) || overlaps(W, need, C, c_bytes))
+    return SGEMM_MI355_ERR_ALIAS;
+  if (tiles_for(*cfg, p.M, p.N) * cfg->threads > (int64_t)UINT32_MAX) return SGEMM_MI355_ERR_EXTENT;
+  const int64_t plane = (int64_t)p.M * p.N;
+  const GemmArgs g{p.M,
+                   p.N,
+                   sp.kchunk,
+                   p.A,
+                   p.lda,
+                   p.B,
+                   p.ldb,
+                   W,
+                   p.N,
+                   1.0f,
+                   0.0f,
+                   p.opA ? (int64_t)sp.kchunk * p.lda : (int64_t)sp.kchunk,
+                   p.opB ? (int64_t)sp.kchunk : (int64_t)sp.kchunk * p.ldb,
+                   plane,
+                   sp.splits,
+                   sp.k_last};
+  if (launch_batches(cfg, g, false, stream) != hipSuccess) return SGEMM_MI355_ERR_LAUNCH;
+  if (launch_splitk_reduce(W, sp.splits, p.M, p.N, p.alpha, p.beta, C, p.ldc, stream) != hipSuccess)
+    return SGEMM_MI355_ERR_LAUNCH;
   return SGEMM_MI355_OK;
+}
+
+// Split count and tile for a problem: no split while one chunk already gives
+// at least two workgroups per compute unit; otherwise the smallest power of
+// two (chunks of at least 256 values of k) that reaches that.
+void select_splitk(int opA, int opB, int M, int N, int K, int* splits, int* config) {
+  int s = 1;
+  for (int cand = 1; cand <= 32; cand *= 2) {
+    if (cand > 1 && (int64_t)K < 256LL * cand) break;
+    s = cand;
+    const int id = rule_select(opA, opB, M, N, cand);
+    if (tiles_for(*config_at(id), M, N) * cand >= 2 * kCompute) break;
+  }
+  const SplitPlan sp = plan_splits(K, s);
+  *splits = sp.splits;
+  *config = sp.splits == 1 ? select_mfma(opA, opB, M, N, K, 1) : rule_select(opA, opB, M, N, sp.splits);
 }
 
 Problem plain(int M, int N, int K, const float* A, int lda, const float* B, int ldb, const float* C,
@@ -237,6 +338,37 @@ int sgemm_mi355_strided_batched_with_config(int opA, int opB, int M, int N, int 
                                             hipStream_t stream, int config) {
   const Problem p{opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc, strideC, batch};
   return run(p, C, stream, config);
+}
+
+size_t sgemm_mi355_splitk_workspace_size(int M, int N, int K, int splits) {
+  if (M <= 0 || N <= 0 || K <= 0 || splits < 1 || splits > kMaxSplits) return 0;
+  return (size_t)splitk_bytes(M, N, plan_splits(K, splits).splits);
+}
+
+int sgemm_mi355_splitk(int opA, int opB, int M, int N, int K, float alpha, const float* A, int lda,
+                       const float* B, int ldb, float beta, float* C, int ldc, int splits,
+                       float* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const Problem p{opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1};
+  if (validate(p) != SGEMM_MI355_OK) return validate(p);
+  const SplitPlan sp = plan_splits(K, splits);
+  const int config = sp.splits > 1 ? rule_select(opA, opB, M, N, sp.splits) : select_for(p);
+  return run_splitk(p, C, splits, workspace, workspace_bytes, stream, config);
+}
+
+int sgemm_mi355_splitk_with_config(int opA, int opB, int M, int N, int K, float alpha,
+                                   const float* A, int lda, const float* B, int ldb, float beta,
+                                   float* C, int ldc, int splits, float* workspace,
+                                   size_t workspace_bytes, hipStream_t stream, int config) {
+  const Problem p{opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1};
+  return run_splitk(p, C, splits, workspace, workspace_bytes, stream, config);
+}
+
+int sgemm_mi355_select_splitk(int opA, int opB, int M, int N, int K, int* splits, int* config) {
+  if ((opA != 0 && opA != 1) || (opB != 0 && opB != 1)) return SGEMM_MI355_ERR_OP;
+  if (M < 0 || N < 0 || K < 0) return SGEMM_MI355_ERR_DIM;
+  if (!splits || !config) return SGEMM_MI355_ERR_NULL;
+  select_splitk(opA, opB, M, N, K, splits, config);
+  return SGEMM_MI355_OK;
 }
 
 int sgemm_mi355_validate(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
@@ -308,10 +440,11 @@ const char* sgemm_mi355_strerror(int code) {
     case SGEMM_MI355_ERR_ALIGN: return "a matrix pointer is not 4-byte aligned";
     case SGEMM_MI355_ERR_STRIDE: return "a batch stride is negative, or batch entries of C overlap";
     case SGEMM_MI355_ERR_OP: return "an operand op is neither SGEMM_MI355_OP_N nor SGEMM_MI355_OP_T";
+    case SGEMM_MI355_ERR_WORKSPACE: return "the split-K workspace is smaller than sgemm_mi355_splitk_workspace_size";
     default: return "unknown error code";
   }
 }
 
-const char* sgemm_mi355_version(void) { return "0.2.0"; }
+const char* sgemm_mi355_version(void) { return "0.3.0"; }
 
 }  // extern "C"

@@ -24,6 +24,7 @@ struct GemmArgs {
   float alpha, beta;
   int64_t strideA, strideB, strideC;
   int batch;
+  int k_last;  // K of the last batch entry of the launch (split-K chunks); K otherwise
 };
 
 using LaunchFn = hipError_t (*)(const GemmArgs&, hipStream_t);
@@ -50,6 +51,12 @@ extern const int kNumValuConfigs;
 // (the K == 0 or alpha == 0 case); beta == 0 writes +0 without reading C.
 // Defined in kernels_valu.hip.
 hipError_t launch_scale_c(const GemmArgs& g, hipStream_t s);
+
+// C = alpha * sum_{s < splits} W_s + beta * C over M x N, the W_s dense M x N
+// partial products (row stride N) at W + s*M*N, summed in ascending s.
+// Defined in kernels_valu.hip.
+hipError_t launch_splitk_reduce(const float* W, int splits, int M, int N, float alpha, float beta,
+                                float* C, int64_t ldc, hipStream_t s);
 
 // Batch entries per launch: each launch covers one batch entry per grid.y
 // index, and larger batches are split into several launches on the host.

@@ -41,6 +41,8 @@
 #ifndef SGEMM_MI355_H
 #define SGEMM_MI355_H
 
+#include <stddef.h>
+
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -58,6 +60,7 @@ extern "C" {
 #define SGEMM_MI355_ERR_ALIGN (-8)    /* a pointer is not 4-byte aligned */
 #define SGEMM_MI355_ERR_STRIDE (-9)   /* a batch stride is negative, or batch entries of C overlap */
 #define SGEMM_MI355_ERR_OP (-10)      /* an op argument is neither OP_N nor OP_T */
+#define SGEMM_MI355_ERR_WORKSPACE (-11) /* split-K workspace smaller than required */
 
 /* Operand ops for the general entry points (row-major storage throughout). */
 #define SGEMM_MI355_OP_N 0 /* op(X) = X */
@@ -150,6 +153,49 @@ int sgemm_mi355_strided_batched_with_config(int opA, int opB, int M, int N, int 
                                             int batch, hipStream_t stream, int config);
 
 /*
+ * Split-K form of sgemm_mi355_ex for problems whose M x N grid of block tiles
+ * is too small to fill the chip: K is cut into up to `splits` chunks (each a
+ * multiple of 32 values of k, the last one taking the rest; fewer chunks when
+ * K is small). Chunk s writes op(A)[:, chunk s] . op(B)[chunk s, :] into a
+ * dense M x N FP32 partial (row stride N) in `workspace`; a second kernel then
+ * sets C = alpha * (sum of the partials, added in ascending chunk order) +
+ * beta * C. The fixed order makes the result independent of timing (repeated
+ * calls give identical bits); it rounds differently from the unsplit product
+ * but stays within the same error bound, and integer-valued products are
+ * exact. `workspace` is device memory owned by the caller, at least
+ * sgemm_mi355_splitk_workspace_size(M, N, K, splits) bytes, 4-byte aligned,
+ * not overlapping A, B or C; it is not needed (may be NULL) when that size is
+ * 0. Both kernels are enqueued on `stream`; the workspace may be reused once
+ * work ordered after them on that stream starts. 1 <= splits <= 256, else
+ * SGEMM_MI355_ERR_DIM; a short workspace gives SGEMM_MI355_ERR_WORKSPACE.
+ */
+int sgemm_mi355_splitk(int opA, int opB, int M, int N, int K, float alpha,
+                       const float *A, int lda, const float *B, int ldb,
+                       float beta, float *C, int ldc, int splits,
+                       float *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes sgemm_mi355_splitk needs (0: no split, none needed). */
+size_t sgemm_mi355_splitk_workspace_size(int M, int N, int K, int splits);
+
+/*
+ * sgemm_mi355_splitk with the tile configuration of the chunk products
+ * forced to `config` (built for this opA/opB pair). For tuning and tests.
+ */
+int sgemm_mi355_splitk_with_config(int opA, int opB, int M, int N, int K, float alpha,
+                                   const float *A, int lda, const float *B, int ldb,
+                                   float beta, float *C, int ldc, int splits,
+                                   float *workspace, size_t workspace_bytes,
+                                   hipStream_t stream, int config);
+
+/*
+ * Split count and tile configuration the library suggests for a problem
+ * (host only): no split while the tile grid alone gives at least two
+ * workgroups per compute unit, else the smallest power of two that does,
+ * with chunks of at least 256 values of k. Writes *splits and *config.
+ */
+int sgemm_mi355_select_splitk(int opA, int opB, int M, int N, int K, int *splits, int *config);
+
+/*
  * Argument validation alone: returns the code the entry points above would
  * return for these arguments before touching the GPU (0 if they would run).
  * Pure host code; makes no HIP call.
@@ -210,7 +256,7 @@ int sgemm_mi355_tile_map(int bid, int tiles_m, int tiles_n, int group_m, int *tm
 /* Static message for an error code (never NULL). */
 const char *sgemm_mi355_strerror(int code);
 
-/* Library version string, e.g. "0.2.0". */
+/* Library version string, e.g. "0.3.0". */
 const char *sgemm_mi355_version(void);
 
 #ifdef __cplusplus

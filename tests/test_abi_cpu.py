@@ -47,7 +47,8 @@ def test_error_codes_match_header():
     text = open(os.path.join(ROOT, "include", "sgemm_mi355.h")).read()
     codes = dict((k, int(v)) for k, v in re.findall(r"#define SGEMM_MI355_(\w+) \(?(-?\d+)\)?", text))
     assert codes["OK"] == sg.OK
-    for name in ("DIM", "LD", "NULL", "ALIAS", "EXTENT", "LAUNCH", "CONFIG", "ALIGN", "STRIDE", "OP"):
+    for name in ("DIM", "LD", "NULL", "ALIAS", "EXTENT", "LAUNCH", "CONFIG", "ALIGN", "STRIDE", "OP",
+                 "WORKSPACE"):
         assert codes["ERR_" + name] == getattr(sg, "ERR_" + name)
         assert sg.strerror(codes["ERR_" + name]) != sg.strerror(12345)
     assert sg.strerror(0) == "success"
@@ -111,9 +112,10 @@ def test_config_metadata():
         bm, bn, bk, threads = sg.sgemm_mi355_config_info(i)
         assert f"{bm}x{bn}x{bk}" in name
         assert threads % 64 == 0 and 64 <= threads <= 1024
-        assert name.startswith(("mfma32_", "valu8x8_"))
-        if name.startswith("valu8x8_"):
-            assert threads == (bm // 8) * (bn // 8)
+        assert name.startswith(("mfma32_", "valu"))
+        if name.startswith("valu"):
+            tm = int(name[4:name.index("x")])
+            assert threads == (bm // tm) * (bn // 8)
     assert sg.sgemm_mi355_version().count(".") == 2
 
 
@@ -241,3 +243,40 @@ def test_binding_leading_dimension_of_torch_tensors():
         _ld(torch.zeros(4, 8).t(), "x")
     with pytest.raises(ValueError):
         _ld(torch.zeros(2, 3, 4), "x")
+
+
+
+# ---- split-K: sizing and validation (no kernel runs) -------------------------
+
+def test_splitk_workspace_size():
+    ws = sg.sgemm_mi355_splitk_workspace_size
+    assert ws(100, 50, 1000, 1) == 0                 # no split
+    assert ws(100, 50, 1000, 4) == 4 * 4 * 100 * 50  # chunks of 256 -> 4 partials
+    assert ws(100, 50, 64, 8) == 2 * 4 * 100 * 50    # chunks of at least 32 -> 2 partials
+    assert ws(100, 50, 20, 8) == 0                   # K below one chunk: no split
+    assert ws(0, 50, 1000, 4) == 0 and ws(100, 50, 1000, 0) == 0 and ws(100, 50, 1000, 257) == 0
+
+
+def test_splitk_rejects_bad_arguments_before_any_hip_call():
+    W = 0x40000000
+    f = sg.sgemm_mi355_splitk
+    assert f(0, 0, 100, 50, 1000, 1.0, A0, 1000, B0, 50, 0.0, C0, 50, 0, W, 10 ** 7, 0) == sg.ERR_DIM
+    assert f(0, 0, 100, 50, 1000, 1.0, A0, 1000, B0, 50, 0.0, C0, 50, 300, W, 10 ** 7, 0) == sg.ERR_DIM
+    need = sg.sgemm_mi355_splitk_workspace_size(100, 50, 1000, 4)
+    assert f(0, 0, 100, 50, 1000, 1.0, A0, 1000, B0, 50, 0.0, C0, 50, 4, W, need - 4, 0) == sg.ERR_WORKSPACE
+    assert f(0, 0, 100, 50, 1000, 1.0, A0, 1000, B0, 50, 0.0, C0, 50, 4, 0, need, 0) == sg.ERR_NULL
+    assert f(0, 0, 100, 50, 1000, 1.0, A0, 1000, B0, 50, 0.0, C0, 50, 4, W + 2, need, 0) == sg.ERR_ALIGN
+    assert f(0, 0, 100, 50, 1000, 1.0, A0, 1000, B0, 50, 0.0, C0, 50, 4, C0 + 400, need, 0) == sg.ERR_ALIAS
+    assert f(0, 0, 100, 50, 1000, 1.0, A0, 1000, B0, 50, 0.0, C0, 50, 4, A0 + 4000, need, 0) == sg.ERR_ALIAS
+
+
+def test_select_splitk():
+    for opA, opB in [(0, 0), (1, 1)]:
+        sp, cid = sg.sgemm_mi355_select_splitk(opA, opB, 8192, 8192, 8192)
+        assert sp == 1 and sg.sgemm_mi355_config_ops(cid) == (opA, opB)
+        sp, cid = sg.sgemm_mi355_select_splitk(opA, opB, 256, 256, 8192)
+        assert sp > 1 and sg.sgemm_mi355_config_ops(cid) == (opA, opB)
+    sp, _ = sg.sgemm_mi355_select_splitk(0, 0, 256, 256, 300)
+    assert sp == 1                                    # chunks would be shorter than 256
+    with pytest.raises(sg.SgemmError):
+        sg.sgemm_mi355_select_splitk(2, 0, 1, 1, 1)

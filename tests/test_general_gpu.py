@@ -180,3 +180,67 @@ def test_batch_beyond_one_grid():
     # every entry: the row sums of C_b equal A_b.(B_b.1) exactly (small integers)
     np.testing.assert_array_equal(out.sum(axis=2).astype(np.float64),
                                   np.einsum("bmk,bk->bm", An.astype(np.float64), Bn.astype(np.float64).sum(axis=2)))
+
+
+# ---------------------------------------------------------------- split-K
+
+def run_splitk(opA, opB, alpha, A, B, beta, C0, splits, config=None, poison=True):
+    M, N = C0.shape
+    K = A.shape[0] if opA else A.shape[1]
+    need = sg.sgemm_mi355_splitk_workspace_size(M, N, K, splits)
+    ws = torch.full(((need + 3) // 4 + 1,), float("nan") if poison else 0.0, device="cuda")
+    print(f"[gpu] splitk op={opA}{opB} M={M} N={N} K={K} splits={splits} config={config}", flush=True)
+    Cd = torch.from_numpy(C0.copy()).to("cuda")
+    sg.gemm_splitk(torch.from_numpy(A).to("cuda"), torch.from_numpy(B).to("cuda"), Cd, splits=splits,
+                   opA=opA, opB=opB, alpha=alpha, beta=beta, workspace=ws, config=config)
+    torch.cuda.synchronize()
+    return Cd.cpu().numpy()
+
+
+@pytest.mark.parametrize("opA,opB", OPS)
+@pytest.mark.parametrize("splits", [2, 3, 4, 8, 16])
+def test_splitk_integer_exact(opA, opB, splits):
+    """Chunks are multiples of 32; K = 1537 leaves a short last chunk."""
+    M, N, K = 197, 131, 1537
+    A, B, C0 = case(opA, opB, M, N, K, splits * 5 + opA + 2 * opB, "int4")
+    for alpha, beta in [(1.0, 0.0), (2.0, -3.0)]:
+        C = run_splitk(opA, opB, alpha, A, B, beta, C0, splits)
+        np.testing.assert_array_equal(C, oracle_ex(opA, opB, alpha, A, B, beta, C0))
+
+
+@pytest.mark.parametrize("opA,opB", OPS)
+def test_splitk_float_within_bound_and_deterministic(opA, opB):
+    M, N, K = 256, 320, 4100
+    A, B, C0 = case(opA, opB, M, N, K, 41, "normal")
+    P, S = oracle.sgemm_ex_f64_abs(opA, opB, A, B)
+    C = run_splitk(opA, opB, 0.5, A, B, -1.5, C0, 8)
+    ok, worst, rel = oracle.check_ex_against_f64(C, 0.5, P, S, -1.5, C0, K)
+    assert ok, f"bound ratio {worst:.3g}, rel {rel:.3g}"
+    for _ in range(4):
+        np.testing.assert_array_equal(run_splitk(opA, opB, 0.5, A, B, -1.5, C0, 8, poison=False), C)
+
+
+def test_splitk_every_plain_config_and_suggested_split():
+    M, N, K = 130, 97, 2050
+    A, B, _ = workloads.draw(M, N, K, 17, "int4")
+    A, B = workloads.as_numpy(A), workloads.as_numpy(B)
+    C0 = np.zeros((M, N), np.float32)
+    want = oracle.sgemm_f32(A, B)
+    for cid in range(sg.sgemm_mi355_num_configs()):
+        if sg.sgemm_mi355_config_ops(cid) != (0, 0):
+            continue
+        np.testing.assert_array_equal(run_splitk(0, 0, 1.0, A, B, 0.0, C0, 5, config=cid), want)
+    # the library's own choice of split and tile
+    Cd = sg.gemm_splitk(torch.from_numpy(A).to("cuda"), torch.from_numpy(B).to("cuda"))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(Cd.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("w", [workloads.BY_NAME["square1024"], workloads.BY_NAME["ragged3001x2047x1537"]],
+                         ids=lambda w: w.name)
+def test_splitk_on_workloads(w):
+    A, B = workloads.inputs(w, integer=True)
+    A, B = workloads.as_numpy(A), workloads.as_numpy(B)
+    C = run_splitk(0, 0, 1.0, A, B, 0.0, np.zeros((w.M, w.N), np.float32), 4)
+    G.check_exact_checksums(C, A, B)
+    G.check_exact(C, A, B, rows=G.band_sample(w.M, 128, 5), cols=G.band_sample(w.N, 128, 6))
