@@ -76,6 +76,7 @@ def main(argv=None):
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kinds", default="mfma", help="mfma, valu or mfma,valu")
+    ap.add_argument("--splitk", default="", help="split counts to time with sgemm_mi355_splitk, e.g. 2,4,8")
     ap.add_argument("--json", default=None)
     ap.add_argument("--table", default=None)
     args = ap.parse_args(argv)
@@ -95,6 +96,24 @@ def main(argv=None):
             row["times_ms"][names[cid]] = ms
             print(f"{M}x{N}x{K} {names[cid]:28s} {ms:9.4f} ms {2 * M * N * K / ms / 1e9:9.2f} TFLOP/s",
                   flush=True)
+        for sp in [int(x) for x in args.splitk.split(",") if x]:
+            need = sg.sgemm_mi355_splitk_workspace_size(M, N, K, sp)
+            ws = torch.empty((need + 3) // 4 + 1, device="cuda")
+            stream = torch.cuda.current_stream()
+            run = lambda: sg.gemm_splitk(Ad, Bd, C, splits=sp, workspace=ws, stream=stream)
+            for _ in range(args.warmup):
+                run()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.reps)]
+            for s0, e0 in ev:
+                s0.record(stream)
+                run()
+                e0.record(stream)
+            torch.cuda.synchronize()
+            ms = statistics.median(s0.elapsed_time(e0) for s0, e0 in ev)
+            row.setdefault("splitk_ms", {})[sp] = ms
+            print(f"{M}x{N}x{K} splitk={sp:<3d} (gemm + reduce)        {ms:9.4f} ms "
+                  f"{2 * M * N * K / ms / 1e9:9.2f} TFLOP/s", flush=True)
         mfma = {n: t for n, t in row["times_ms"].items() if n.startswith("mfma")}
         if mfma:
             row["best"] = min(mfma, key=mfma.get)

@@ -222,7 +222,7 @@ def test_splitk_float_within_bound_and_deterministic(opA, opB):
 
 def test_splitk_every_plain_config_and_suggested_split():
     M, N, K = 130, 97, 2050
-    A, B, _ = workloads.draw(M, N, K, 17, "int4")
+    A, B = workloads.draw(M, N, K, 17, "int4")
     A, B = workloads.as_numpy(A), workloads.as_numpy(B)
     C0 = np.zeros((M, N), np.float32)
     want = oracle.sgemm_f32(A, B)
