@@ -35,16 +35,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+KERNEL_SOURCES = {"mfma": ("kernels_mfma.hip", "sgemm_internal.h"),
+                  "valu": ("kernels_valu.hip", "sgemm_internal.h")}
+
+
+def kernel_source_hash(kind: str = "mfma") -> str:
+    """Hash of the source files that define the kind's GEMM kernels: counter
+    figures taken on other sources no longer describe the kernel."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_fp32_matrix_02_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[kind]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, config_name: str):
+def stored_traffic(workload: str, config_name: str, kind: str = "mfma"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -53,7 +59,7 @@ def stored_traffic(workload: str, config_name: str):
     with open(path) as f:
         table = json.load(f)
     e = table.get(f"{workload}/{config_name}")
-    if not e or e.get("kernel_source_hash") != kernel_source_hash():
+    if not e or e.get("kernel_source_hash") != kernel_source_hash(kind):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -69,8 +75,12 @@ def time_gpu(w, steps: int, warmup: int, kind: str, config, warmup_ms: float = 0
     Cd = torch.empty((w.M, w.ldc), dtype=torch.float32, device="cuda")
     Av, Bv, Cv = Ad[:, :w.K], Bd[:, :w.N], Cd[:, :w.N]
     stream = torch.cuda.current_stream()
-    cid = config if config is not None else (
-        sg.sgemm_mi355_select_config(w.M, w.N, w.K) if kind == "mfma" else None)
+    if config is not None:
+        cid = config
+    elif kind == "mfma":
+        cid = sg.sgemm_mi355_select_config(w.M, w.N, w.K)
+    else:
+        cid = sg.sgemm_mi355_select_config_valu(w.M, w.N, w.K)
 
     def step():
         sg.matmul(Av, Bv, out=Cv, kind=kind, config=cid, stream=stream)
@@ -95,7 +105,7 @@ def time_gpu(w, steps: int, warmup: int, kind: str, config, warmup_ms: float = 0
     wall = time.perf_counter() - t0
     per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]  # ms
     total_ms = starts[0].elapsed_time(ends[-1])
-    name = sg.sgemm_mi355_config_name(cid) if cid is not None else "valu(default)"
+    name = sg.sgemm_mi355_config_name(cid)
     return {
         "ms_per_step": total_ms / steps,
         "mean_launch_ms": sum(per_launch) / steps,
@@ -211,7 +221,7 @@ def main():
                      "frac_fp32_mfma_peak": round(va / (PEAK_MFMA_TFLOPS * 1e3), 4)})
         log(f"[bench] also {wa.name}: {va:.1f} GFLOP/s ({ra['config_name']})")
 
-    traffic = stored_traffic(w.name, r["config_name"]) if args.kind == "mfma" else None
+    traffic = stored_traffic(w.name, r["config_name"], args.kind)
     out = {
         "metric": "SGEMM GFLOP/s (FP32) at N=4096/8192; % of MI355X FP32 peak",
         "value": round(value, 1),
@@ -232,9 +242,9 @@ def main():
         "frac_fp32_vector_peak": round(value / (PEAK_VECTOR_TFLOPS * 1e3), 4),
         "peaks_tflops": {"fp32_mfma": PEAK_MFMA_TFLOPS, "fp32_vector": PEAK_VECTOR_TFLOPS},
         "roofline": {
-            "bound": "mfma",
+            "bound": "mfma" if args.kind == "mfma" else "alu",
             "achieved": round(achieved, 2),
-            "peak": PEAK_MFMA_TFLOPS,
+            "peak": PEAK_MFMA_TFLOPS if args.kind == "mfma" else PEAK_VECTOR_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
             "traffic": traffic,

@@ -63,6 +63,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sgemm_mi355_validate_ex.argtypes = [_I, _I, _I, _I, _I, _F, _P, _I, _LL, _P, _I, _LL, _F, _P,
                                             _I, _LL, _I]
     lib.sgemm_mi355_select_config_ex.argtypes = [_I] * 6
+    lib.sgemm_mi355_select_config_valu.argtypes = [_I] * 3
     lib.sgemm_mi355_config_ops.argtypes = [_I, ctypes.POINTER(_I), ctypes.POINTER(_I)]
     lib.sgemm_mi355_select_config.argtypes = [_I, _I, _I]
     lib.sgemm_mi355_num_configs.argtypes = []
@@ -79,7 +80,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                  "sgemm_mi355_tile_map", "sgemm_mi355_ex", "sgemm_mi355_strided_batched",
                  "sgemm_mi355_strided_batched_with_config", "sgemm_mi355_validate_ex",
                  "sgemm_mi355_select_config_ex", "sgemm_mi355_config_ops", "sgemm_mi355_splitk",
-                 "sgemm_mi355_splitk_with_config", "sgemm_mi355_select_splitk"):
+                 "sgemm_mi355_splitk_with_config", "sgemm_mi355_select_splitk",
+                 "sgemm_mi355_select_config_valu"):
         getattr(lib, name).restype = _I
     _lib = lib
     return lib
@@ -146,6 +148,10 @@ def sgemm_mi355_validate_ex(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, s
                             strideC, batch) -> int:
     return load().sgemm_mi355_validate_ex(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB,
                                           beta, C, ldc, strideC, batch)
+
+
+def sgemm_mi355_select_config_valu(M, N, K) -> int:
+    return load().sgemm_mi355_select_config_valu(M, N, K)
 
 
 def sgemm_mi355_select_config_ex(opA, opB, M, N, K, batch) -> int:

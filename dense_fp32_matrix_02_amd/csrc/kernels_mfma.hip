@@ -333,6 +333,11 @@ hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
   {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, KIND_MFMA, BM, BN, BK, 64 * WM * WN, \
    TA, TB, &launch_mfma<MfmaCfg<BM, BN, BK, WM, WN, LA, LB, 4>>}
 #define SGEMM_MFMA_N(BM, BN, BK, WM, WN) SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, KC, MC, 0, 0, "")
+// Plain configuration walking the tile grid in bands of 8 tile rows (_g8)
+// instead of 4.
+#define SGEMM_MFMA_G8(BM, BN, BK, WM, WN)                                                       \
+  {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_g8", KIND_MFMA, BM, BN, BK, 64 * WM * WN, 0, 0, \
+   &launch_mfma<MfmaCfg<BM, BN, BK, WM, WN, KC, MC, 8>>}
 #define SGEMM_MFMA_K(BM, BN, BK, WM, WN) SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, KC, KM, 0, 0, "_bk")
 #define SGEMM_MFMA_OPS(BM, BN, BK, WM, WN)                                  \
   SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, MC, MC, 1, 0, "_tn"),                  \
@@ -354,6 +359,7 @@ KernelConfig kMfmaConfigs[] = {
     SGEMM_MFMA_K(256, 128, 32, 2, 4),
     SGEMM_MFMA_N(256, 128, 16, 4, 2),
     SGEMM_MFMA_N(256, 128, 32, 4, 2),
+    SGEMM_MFMA_G8(256, 128, 16, 4, 2),
     // medium tiles: grid fill on mid-sized and ragged problems
     SGEMM_MFMA_N(128, 128, 16, 2, 2),
     SGEMM_MFMA_N(128, 128, 32, 2, 2),

@@ -37,9 +37,12 @@ __device__ __forceinline__ f32x4 ldg4(const float* p) {
   return v;
 }
 
-template <int BM_, int BN_, int BK_, int TM_, int GROUP_M_>
+template <int BM_, int BN_, int BK_, int TM_, int GROUP_M_, int WAVES_>
 struct ValuCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, GROUP_M = GROUP_M_;
+  // Minimum waves per SIMD the register allocation must allow (the occupancy
+  // bound GPU Parallel Book section 9.6 sweeps with __launch_bounds__).
+  static constexpr int WAVES = WAVES_;
   static constexpr int TM = TM_, TN = 8;         // microtile per thread
   static constexpr int RG = TM / 4, CG = TN / 4;  // groups of four rows / columns
   static constexpr int TX = BN / TN, TY = BM / TM;
@@ -59,7 +62,8 @@ struct ValuCfg {
 };
 
 template <class Cfg>
-__global__ void __launch_bounds__(Cfg::NT) valu_gemm_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::WAVES)))
+valu_gemm_kernel(GemmArgs g) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
   constexpr int SA = Cfg::SA, SB = Cfg::SB;
   constexpr int AP = Cfg::A_PASSES, BP = Cfg::B_PASSES;
@@ -232,17 +236,20 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
 
 }  // namespace
 
-// Name: valu<TM>x8_<BM>x<BN>x<BK>: microtile TM x 8 per thread, block tile BM x BN.
-#define SGEMM_VALU_CFG(BM, BN, BK, TM)                                                            \
-  {"valu" #TM "x8_" #BM "x" #BN "x" #BK, KIND_VALU, BM, BN, BK, (BM / TM) * (BN / 8), 0, 0, \
-   &launch_valu<ValuCfg<BM, BN, BK, TM, 4>>}
+// Name: valu<TM>x8_<BM>x<BN>x<BK>[_o<W>]: microtile TM x 8 per thread, block
+// tile BM x BN, registers bounded for at least W waves per SIMD (default 1).
+#define SGEMM_VALU_CFG(BM, BN, BK, TM, W, SUFFIX)                                                        \
+  {"valu" #TM "x8_" #BM "x" #BN "x" #BK SUFFIX, KIND_VALU, BM, BN, BK, (BM / TM) * (BN / 8), 0, 0, \
+   &launch_valu<ValuCfg<BM, BN, BK, TM, 4, W>>}
 
 KernelConfig kValuConfigs[] = {
-    SGEMM_VALU_CFG(128, 128, 8, 8),
-    SGEMM_VALU_CFG(128, 128, 16, 8),
-    SGEMM_VALU_CFG(64, 64, 16, 8),
-    SGEMM_VALU_CFG(256, 128, 8, 16),
-    SGEMM_VALU_CFG(128, 128, 8, 16),
+    SGEMM_VALU_CFG(128, 128, 8, 8, 1, ""),
+    SGEMM_VALU_CFG(128, 128, 8, 8, 5, "_o5"),
+    SGEMM_VALU_CFG(128, 128, 16, 8, 1, ""),
+    SGEMM_VALU_CFG(128, 128, 16, 8, 4, "_o4"),
+    SGEMM_VALU_CFG(64, 64, 16, 8, 1, ""),
+    SGEMM_VALU_CFG(256, 128, 8, 16, 1, ""),
+    SGEMM_VALU_CFG(256, 128, 8, 16, 3, "_o3"),
 };
 const int kNumValuConfigs = sizeof(kValuConfigs) / sizeof(kValuConfigs[0]);
 

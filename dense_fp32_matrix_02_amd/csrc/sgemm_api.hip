@@ -6,6 +6,7 @@
 #include "sgemm_mi355.h"
 
 #include <climits>
+#include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -72,27 +73,52 @@ int rule_select(int opA, int opB, int M, int N, int batch) {
   return last;
 }
 
+// Table lookup for the plain product: the measured entry of the same shape,
+// else the measured entry nearest in (log M, log N, log K) provided it lies
+// within a factor of two in each dimension; -1 when none qualifies.
+int table_select(int M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0) return -1;
+  int best = -1;
+  double best_d = 1e30;
+  for (const ShapeEntry* e = kShapeTable; e->config; ++e) {
+    const int id = config_id(e->config);
+    if (id < 0) continue;
+    if (e->M == M && e->N == N && e->K == K) return id;
+    const double dm = std::fabs(std::log2((double)M / e->M));
+    const double dn = std::fabs(std::log2((double)N / e->N));
+    const double dk = std::fabs(std::log2((double)K / e->K));
+    if (dm > 1.0 || dn > 1.0 || dk > 1.0) continue;
+    const double d = dm + dn + dk;
+    if (d < best_d) {
+      best_d = d;
+      best = id;
+    }
+  }
+  return best;
+}
+
 int select_mfma(int opA, int opB, int M, int N, int K, int batch) {
-  if (!opA && !opB && batch == 1)
-    for (const ShapeEntry* e = kShapeTable; e->config; ++e)
-      if (e->M == M && e->N == N && e->K == K) {
-        const int id = config_id(e->config);
-        if (id >= 0) return id;
-      }
+  if (!opA && !opB && batch == 1) {
+    const int id = table_select(M, N, K);
+    if (id >= 0) return id;
+  }
   return rule_select(opA, opB, M, N, batch);
 }
 
-// Vector-kernel configurations: largest tile with one workgroup per CU.
+// Vector-kernel configurations the selection considers, largest block tile
+// first (the fastest measured configuration of each tile size): the largest
+// that still gives one workgroup per compute unit, else the smallest.
+const char* const kValuRuleTiles[] = {"valu8x8_128x128x8", "valu8x8_64x64x16"};
+
 int select_valu(int M, int N) {
-  int best = -1, smallest = -1;
-  int64_t best_area = -1, small_area = INT64_MAX;
-  for (int i = kNumMfmaConfigs; i < num_configs(); ++i) {
-    const KernelConfig* c = config_at(i);
-    const int64_t area = (int64_t)c->bm * c->bn;
-    if (area < small_area) { small_area = area; smallest = i; }
-    if (tiles_for(*c, M, N) >= kCompute && area > best_area) { best = i; best_area = area; }
+  int last = -1;
+  for (const char* name : kValuRuleTiles) {
+    const int id = config_id(name);
+    if (id < 0) continue;
+    last = id;
+    if (tiles_for(*config_at(id), M, N) >= kCompute) return id;
   }
-  return best >= 0 ? best : smallest;
+  return last;
 }
 
 bool overlaps(const void* p, unsigned __int128 pbytes, const void* q, unsigned __int128 qbytes) {
@@ -386,6 +412,11 @@ int sgemm_mi355_validate_ex(int opA, int opB, int M, int N, int K, float alpha, 
 int sgemm_mi355_select_config(int M, int N, int K) {
   if (M < 0 || N < 0 || K < 0) return SGEMM_MI355_ERR_DIM;
   return select_mfma(0, 0, M, N, K, 1);
+}
+
+int sgemm_mi355_select_config_valu(int M, int N, int K) {
+  if (M < 0 || N < 0 || K < 0) return SGEMM_MI355_ERR_DIM;
+  return select_valu(M, N);
 }
 
 int sgemm_mi355_select_config_ex(int opA, int opB, int M, int N, int K, int batch) {

@@ -29,10 +29,10 @@ TABLE_HEADER = """\
 // Tile-configuration table: which kernel configuration each problem shape
 // uses. The best tile is an empirical question (CUDA Handbook section 17.3:
 // the microtile is chosen by sweeping; GPU Parallel Book section 9.6: the
-// occupancy setting is found by measurement), so exact-shape entries record
-// the fastest configuration measured on MI355X for that shape, and other
-// shapes fall back to the rule in sgemm_api.hip (largest block tile that
-// still gives one workgroup per compute unit).
+// occupancy setting is found by measurement), so each entry records the
+// fastest configuration measured on MI355X for one shape. A shape without
+// its own entry takes the nearest measured shape (in log M, log N, log K,
+// within a factor of two in each), else the rule in sgemm_api.hip.
 //
 // Written by dense_fp32_matrix_02_amd/tune.py (median of {reps} launches per
 // configuration). Format: {{M, N, K, "configuration name"}}.
@@ -73,6 +73,8 @@ def main(argv=None):
 
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--shapes", default=",".join(f"{w.M}x{w.N}x{w.K}" for w in workloads.WORKLOADS))
+    ap.add_argument("--grid", action="store_true",
+                    help="also measure the grid M, N in {512..8192} (powers of two) x K in {512, 2048, 8192}")
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kinds", default="mfma", help="mfma, valu or mfma,valu")
@@ -86,7 +88,12 @@ def main(argv=None):
     cands = [i for i, n in enumerate(names)
              if n.startswith(tuple(kinds)) and sg.sgemm_mi355_config_ops(i) == (0, 0)]
     results = []
-    for (M, N, K) in parse_shapes(args.shapes):
+    shapes = parse_shapes(args.shapes)
+    if args.grid:
+        sides = [512, 1024, 2048, 4096, 8192]
+        shapes += [(m, n, k) for m in sides for n in sides for k in (512, 2048, 8192)
+                   if (m, n, k) not in shapes]
+    for (M, N, K) in shapes:
         A, B = workloads.draw(M, N, K, 1234, "uniform")
         Ad, Bd = A.to("cuda"), B.to("cuda")
         C = torch.empty((M, N), device="cuda")

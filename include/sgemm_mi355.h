@@ -217,6 +217,9 @@ int sgemm_mi355_validate_ex(int opA, int opB, int M, int N, int K, float alpha,
 /* Configuration id the tile table picks for a problem shape (host only). */
 int sgemm_mi355_select_config(int M, int N, int K);
 
+/* Configuration id sgemm_mi355_valu uses for a problem shape (host only). */
+int sgemm_mi355_select_config_valu(int M, int N, int K);
+
 /* Configuration id chosen for a general/batched problem (host only). */
 int sgemm_mi355_select_config_ex(int opA, int opB, int M, int N, int K, int batch);
 
