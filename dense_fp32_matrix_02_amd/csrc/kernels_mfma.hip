@@ -171,18 +171,31 @@ struct Operand {
   }
 };
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int LA_, int LB_, int GROUP_M_>
+// KG > 1 splits every slab's k range among KG groups of WM x WN waves: group
+// g multiplies k = g*BK/KG .. (g+1)*BK/KG - 1 of each slab into its own
+// accumulators, and the groups' sums are added in ascending g through LDS at
+// the end. All KG*WM*WN waves load the slabs. This keeps several waves per
+// SIMD busy when the tile grid alone gives too few (small and mid-sized
+// problems) without a second pass over C.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int LA_, int LB_, int GROUP_M_, int KG_ = 1>
 struct MfmaCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
   static constexpr int WM = WM_, WN = WN_;  // waves along M and N
+  static constexpr int KG = KG_;            // wave groups sharing each slab's k range
+  static constexpr int KS = BK / KG;        // k values per group per slab
   static constexpr int GROUP_M = GROUP_M_;
-  static constexpr int NT = 64 * WM * WN;
+  static constexpr int NT = 64 * WM * WN * KG;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   static constexpr int FM = WTM / 32, FN = WTN / 32;  // 32x32 blocks per wave
   using OpA = Operand<BM, BK, NT, LA_>;
   using OpB = Operand<BN, BK, NT, LB_>;
-  static constexpr int LDS_BYTES = 4 * 2 * (OpA::FLOATS + OpB::FLOATS);
+  static constexpr int SLAB_FLOATS = 2 * (OpA::FLOATS + OpB::FLOATS);
+  static constexpr int RED_FLOATS = (KG - 1) * BM * BN;  // partial sums of groups 1..KG-1
+  static constexpr int LDS_FLOATS = SLAB_FLOATS > RED_FLOATS ? SLAB_FLOATS : RED_FLOATS;
+  static constexpr int LDS_BYTES = 4 * LDS_FLOATS;
   static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile must be 32x32 blocks");
+  static_assert(KS % 8 == 0 && KS * KG == BK, "each group takes whole 8-deep k steps");
+  static_assert(NT <= 1024, "at most 1024 threads per workgroup");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
 };
 
@@ -193,8 +206,11 @@ __global__ void __launch_bounds__(Cfg::NT) mfma_gemm_kernel(GemmArgs g) {
   using OpA = typename Cfg::OpA;
   using OpB = typename Cfg::OpB;
 
-  __shared__ __attribute__((aligned(16))) float As[2 * OpA::FLOATS];
-  __shared__ __attribute__((aligned(16))) float Bs[2 * OpB::FLOATS];
+  // Two slab buffers of each operand; with KG > 1 the same memory holds the
+  // groups' partial sums after the last slab.
+  __shared__ __attribute__((aligned(16))) float smem[Cfg::LDS_FLOATS];
+  float* const As = smem;
+  float* const Bs = smem + 2 * OpA::FLOATS;
 
   const int M = g.M, N = g.N;
   const int K = (blockIdx.y == gridDim.y - 1) ? g.k_last : g.K;  // last split-K chunk may be short
@@ -204,10 +220,13 @@ __global__ void __launch_bounds__(Cfg::NT) mfma_gemm_kernel(GemmArgs g) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int wm = wave % Cfg::WM, wn = wave / Cfg::WM;
+  const int kg = Cfg::KG == 1 ? 0 : wave / (Cfg::WM * Cfg::WN);  // k group
+  const int wg = wave - kg * (Cfg::WM * Cfg::WN);
+  const int wm = wg % Cfg::WM, wn = wg / Cfg::WM;
   const int l32 = lane & 31, h = lane >> 5;
-  const int a_frag = OpA::frag_offset(wm * Cfg::WTM + l32, h);
-  const int b_frag = OpB::frag_offset(wn * Cfg::WTN + l32, h);
+  // Fragment offsets include the group's first k of the slab.
+  const int a_frag = OpA::frag_offset(wm * Cfg::WTM + l32, h) + kg * Cfg::KS * (OpA::KMAJ ? 1 : OpA::S);
+  const int b_frag = OpB::frag_offset(wn * Cfg::WTN + l32, h) + kg * Cfg::KS * (OpB::KMAJ ? 1 : OpB::S);
   constexpr int A_BLOCK = OpA::KMAJ ? 32 * OpA::S : 32;  // offset between 32-line blocks
   constexpr int B_BLOCK = OpB::KMAJ ? 32 * OpB::S : 32;
   using Full = std::integral_constant<bool, false>;
@@ -242,7 +261,7 @@ __global__ void __launch_bounds__(Cfg::NT) mfma_gemm_kernel(GemmArgs g) {
       const float* as = As + buf * OpA::FLOATS + a_frag;
       const float* bs = Bs + buf * OpB::FLOATS + b_frag;
 #pragma unroll
-      for (int kk = 0; kk < BK; kk += 8) {
+      for (int kk = 0; kk < Cfg::KS; kk += 8) {
         f32x4 af[FM], bf[FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i) af[i] = OpA::frag(as + i * A_BLOCK, kk);
@@ -288,6 +307,33 @@ __global__ void __launch_bounds__(Cfg::NT) mfma_gemm_kernel(GemmArgs g) {
     }
     compute_slab(s & 1);
 
+    // ---- k groups: add the groups' sums in ascending group order ----------
+    if constexpr (Cfg::KG > 1) {
+      constexpr int WAVE_FLOATS = FM * FN * 16 * 64;  // one wave's accumulators
+      __syncthreads();  // every group has finished reading the slab buffers
+      if (kg > 0) {
+        float* red = smem + ((kg - 1) * Cfg::WM * Cfg::WN + wg) * WAVE_FLOATS + lane;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) red[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
+      }
+      __syncthreads();
+      if (kg > 0) return;
+#pragma unroll
+      for (int q = 1; q < Cfg::KG; ++q) {
+        const float* red = smem + ((q - 1) * Cfg::WM * Cfg::WN + wg) * WAVE_FLOATS + lane;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * FN + j) * 16 + r) * 64];
+      }
+    }
+
     // ---- epilogue: masked stores; C is read only when beta != 0 ------------
     float* C = g.C + (int64_t)b * g.strideC;
     const int row0 = m0 + wm * Cfg::WTM + 4 * h;
@@ -326,23 +372,25 @@ hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
 
 }  // namespace
 
-// Name: mfma32_<BM>x<BN>x<BK>_w<WM>x<WN>[_bk][_<ops>]: _bk when B (read
-// line-contiguous) is staged k-major; <ops> = tn, nt or tt names transposed
-// operands (first letter A, second B); no suffix is the plain product.
-#define SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, LA, LB, TA, TB, SUFFIX)                          \
-  {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, KIND_MFMA, BM, BN, BK, 64 * WM * WN, \
-   TA, TB, &launch_mfma<MfmaCfg<BM, BN, BK, WM, WN, LA, LB, 4>>}
-#define SGEMM_MFMA_N(BM, BN, BK, WM, WN) SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, KC, MC, 0, 0, "")
-// Plain configuration walking the tile grid in bands of 8 tile rows (_g8)
-// instead of 4.
-#define SGEMM_MFMA_G8(BM, BN, BK, WM, WN)                                                       \
-  {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_g8", KIND_MFMA, BM, BN, BK, 64 * WM * WN, 0, 0, \
-   &launch_mfma<MfmaCfg<BM, BN, BK, WM, WN, KC, MC, 8>>}
-#define SGEMM_MFMA_K(BM, BN, BK, WM, WN) SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, KC, KM, 0, 0, "_bk")
-#define SGEMM_MFMA_OPS(BM, BN, BK, WM, WN)                                  \
-  SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, MC, MC, 1, 0, "_tn"),                  \
-      SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, KC, KC, 0, 1, "_nt"),              \
-      SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, MC, KC, 1, 1, "_tt")
+// Name: mfma32_<BM>x<BN>x<BK>_w<WM>x<WN>[_g8][_bk][_kg<KG>][_<ops>]: _g8 walks
+// the tile grid in bands of 8 tile rows instead of 4; _bk stages B (read
+// line-contiguous) k-major; _kg<KG> splits each slab's k range among KG wave
+// groups (see MfmaCfg); <ops> = tn, nt or tt names transposed operands (first
+// letter A, second B); no ops suffix is the plain product.
+#define SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, KG, GM, LA, LB, TA, TB, SUFFIX)                       \
+  {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, KIND_MFMA, BM, BN, BK,                \
+   64 * WM * WN * KG, TA, TB, &launch_mfma<MfmaCfg<BM, BN, BK, WM, WN, LA, LB, GM, KG>>}
+#define SGEMM_MFMA_N(BM, BN, BK, WM, WN) SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, 1, 4, KC, MC, 0, 0, "")
+#define SGEMM_MFMA_G8(BM, BN, BK, WM, WN) SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, 1, 8, KC, MC, 0, 0, "_g8")
+#define SGEMM_MFMA_K(BM, BN, BK, WM, WN) SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, 1, 4, KC, KM, 0, 0, "_bk")
+#define SGEMM_MFMA_KG(BM, BN, BK, WM, WN, KG) \
+  SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, KG, 4, KC, MC, 0, 0, "_kg" #KG)
+#define SGEMM_MFMA_OPS_SFX(BM, BN, BK, WM, WN, KG, SFX)                          \
+  SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, KG, 4, MC, MC, 1, 0, SFX "_tn"),            \
+      SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, KG, 4, KC, KC, 0, 1, SFX "_nt"),        \
+      SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, KG, 4, MC, KC, 1, 1, SFX "_tt")
+#define SGEMM_MFMA_OPS(BM, BN, BK, WM, WN) SGEMM_MFMA_OPS_SFX(BM, BN, BK, WM, WN, 1, "")
+#define SGEMM_MFMA_OPS_KG(BM, BN, BK, WM, WN, KG) SGEMM_MFMA_OPS_SFX(BM, BN, BK, WM, WN, KG, "_kg" #KG)
 
 KernelConfig kMfmaConfigs[] = {
     // large block tiles: compute-bound squares
@@ -376,11 +424,25 @@ KernelConfig kMfmaConfigs[] = {
     SGEMM_MFMA_K(64, 64, 64, 2, 2),
     SGEMM_MFMA_N(32, 32, 32, 1, 1),
     SGEMM_MFMA_N(32, 32, 64, 1, 1),
+    // k groups: more waves per tile for grids too small to fill the chip
+    SGEMM_MFMA_KG(128, 128, 32, 2, 2, 2),
+    SGEMM_MFMA_KG(128, 64, 32, 2, 2, 2),
+    SGEMM_MFMA_KG(64, 64, 32, 2, 2, 2),
+    SGEMM_MFMA_KG(64, 64, 64, 2, 2, 2),
+    SGEMM_MFMA_KG(64, 64, 64, 2, 2, 4),
+    SGEMM_MFMA_KG(32, 32, 64, 1, 1, 4),
+    SGEMM_MFMA_KG(32, 32, 128, 1, 1, 4),
+    SGEMM_MFMA_KG(32, 32, 128, 1, 1, 8),
+    SGEMM_MFMA_KG(32, 32, 64, 1, 1, 8),
+    SGEMM_MFMA_KG(32, 32, 256, 1, 1, 16),
+    SGEMM_MFMA_KG(64, 64, 128, 2, 2, 4),
+    SGEMM_MFMA_KG(128, 64, 64, 2, 2, 4),
     // transposed operands (op(A) = A^T and/or op(B) = B^T)
     SGEMM_MFMA_OPS(256, 128, 16, 4, 2),
     SGEMM_MFMA_OPS(128, 64, 16, 2, 2),
-    SGEMM_MFMA_OPS(64, 64, 32, 2, 2),
-    SGEMM_MFMA_OPS(32, 32, 32, 1, 1),
+    SGEMM_MFMA_OPS_KG(64, 64, 64, 2, 2, 2),
+    SGEMM_MFMA_OPS_KG(32, 32, 128, 1, 1, 4),
+    SGEMM_MFMA_OPS_KG(32, 32, 256, 1, 1, 16),
 };
 const int kNumMfmaConfigs = sizeof(kMfmaConfigs) / sizeof(kMfmaConfigs[0]);
 

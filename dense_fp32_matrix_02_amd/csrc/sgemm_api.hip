@@ -25,11 +25,19 @@ struct ShapeEntry {
 constexpr int kCompute = 256;  // compute units on MI355X
 
 // Block tiles the selection rule considers when the table has no entry,
-// largest first (the fastest measured configuration of each tile size).
-const char* const kRuleTiles[] = {"256x128x16_w4x2", "128x64x16_w2x2", "64x64x64_w2x2",
-                                  "32x32x32_w1x1"};
-const char* const kRuleTilesOps[] = {"256x128x16_w4x2", "128x64x16_w2x2", "64x64x32_w2x2",
-                                     "32x32x32_w1x1"};
+// largest first, each with the fewest workgroups (counting batch entries) it
+// needs to be chosen. Below the last threshold, a 32x32 tile with its slabs
+// split among wave groups keeps the SIMDs busy; long K takes the deeper one.
+// Thresholds were fitted to the measured grid the table comes from (about 2%
+// slower than the best configuration there, geometric mean).
+struct RuleTile {
+  const char* tile;
+  int min_wgs;
+};
+const RuleTile kRuleTiles[] = {{"256x128x16_w4x2", 256}, {"128x64x16_w2x2", 768}, {"64x64x64_w2x2_kg2", 256}};
+const char* const kRuleSmall = "32x32x128_w1x1_kg4";
+const char* const kRuleSmallLongK = "32x32x256_w1x1_kg16";
+constexpr int kRuleLongK = 4096;
 
 int num_configs() { return kNumMfmaConfigs + kNumValuConfigs; }
 
@@ -55,22 +63,19 @@ const char* ops_suffix(int opA, int opB) {
   return s[opA][opB];
 }
 
-// The largest rule tile that still gives at least one workgroup per compute
-// unit (counting batch entries), else the smallest.
-int rule_select(int opA, int opB, int M, int N, int batch) {
-  const char* const* tiles = (opA || opB) ? kRuleTilesOps : kRuleTiles;
-  const int n = 4;
+// The first rule tile whose grid reaches its workgroup threshold, else the
+// small k-group tile for this K.
+int rule_select(int opA, int opB, int M, int N, int K, int batch) {
   const int64_t gy = batch < kMaxGridY ? batch : kMaxGridY;
-  int last = -1;
-  for (int i = 0; i < n; ++i) {
-    char name[64];
-    std::snprintf(name, sizeof(name), "mfma32_%s%s", tiles[i], ops_suffix(opA, opB));
+  char name[64];
+  for (const RuleTile& r : kRuleTiles) {
+    std::snprintf(name, sizeof(name), "mfma32_%s%s", r.tile, ops_suffix(opA, opB));
     const int id = config_id(name);
-    if (id < 0) continue;
-    last = id;
-    if (tiles_for(*config_at(id), M, N) * gy >= kCompute) return id;
+    if (id >= 0 && tiles_for(*config_at(id), M, N) * gy >= r.min_wgs) return id;
   }
-  return last;
+  std::snprintf(name, sizeof(name), "mfma32_%s%s", K >= kRuleLongK ? kRuleSmallLongK : kRuleSmall,
+                ops_suffix(opA, opB));
+  return config_id(name);
 }
 
 // Table lookup for the plain product: the measured entry of the same shape,
@@ -102,7 +107,7 @@ int select_mfma(int opA, int opB, int M, int N, int K, int batch) {
     const int id = table_select(M, N, K);
     if (id >= 0) return id;
   }
-  return rule_select(opA, opB, M, N, batch);
+  return rule_select(opA, opB, M, N, K, batch);
 }
 
 // Vector-kernel configurations the selection considers, largest block tile
@@ -293,20 +298,23 @@ int run_splitk(const Problem& p, float* C, int splits, float* W, size_t w_bytes,
   return SGEMM_MI355_OK;
 }
 
-// Split count and tile for a problem: no split while one chunk already gives
-// at least two workgroups per compute unit; otherwise the smallest power of
-// two (chunks of at least 256 values of k) that reaches that.
+// Split count and tile for a problem. Splitting pays only when the unsplit
+// grid leaves compute units idle or under-filled (fewer than two workgroups
+// per CU) and K is long enough that each chunk still does real work: then K
+// is cut into chunks of about kSplitChunk values of k (a power-of-two count).
+// Measured on the tuning shapes: 64x64x65536 and 128x128x16384 gain 5-10x,
+// 256x256x4096 1.8x, 512x512x8192 1.1x; at K <= 1024 the extra pass over C
+// costs more than it saves.
+constexpr int kSplitChunk = 1024;
+
 void select_splitk(int opA, int opB, int M, int N, int K, int* splits, int* config) {
+  const int single = select_mfma(opA, opB, M, N, K, 1);
   int s = 1;
-  for (int cand = 1; cand <= 32; cand *= 2) {
-    if (cand > 1 && (int64_t)K < 256LL * cand) break;
-    s = cand;
-    const int id = rule_select(opA, opB, M, N, cand);
-    if (tiles_for(*config_at(id), M, N) * cand >= 2 * kCompute) break;
-  }
+  if (tiles_for(*config_at(single), M, N) < 2 * kCompute)
+    while (2 * s <= kMaxSplits && (int64_t)K >= 2LL * s * kSplitChunk) s *= 2;
   const SplitPlan sp = plan_splits(K, s);
   *splits = sp.splits;
-  *config = sp.splits == 1 ? select_mfma(opA, opB, M, N, K, 1) : rule_select(opA, opB, M, N, sp.splits);
+  *config = sp.splits == 1 ? single : rule_select(opA, opB, M, N, sp.kchunk, sp.splits);
 }
 
 Problem plain(int M, int N, int K, const float* A, int lda, const float* B, int ldb, const float* C,
@@ -377,7 +385,7 @@ int sgemm_mi355_splitk(int opA, int opB, int M, int N, int K, float alpha, const
   const Problem p{opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1};
   if (validate(p) != SGEMM_MI355_OK) return validate(p);
   const SplitPlan sp = plan_splits(K, splits);
-  const int config = sp.splits > 1 ? rule_select(opA, opB, M, N, sp.splits) : select_for(p);
+  const int config = sp.splits > 1 ? rule_select(opA, opB, M, N, sp.kchunk, sp.splits) : select_for(p);
   return run_splitk(p, C, splits, workspace, workspace_bytes, stream, config);
 }
 

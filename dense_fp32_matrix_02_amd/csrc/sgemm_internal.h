@@ -49,12 +49,12 @@ extern const int kNumValuConfigs;
 
 // C_b = beta * C_b over the M x N block of every batch entry of the launch
 // (the K == 0 or alpha == 0 case); beta == 0 writes +0 without reading C.
-// Defined in kernels_valu.hip.
+// Defined in kernels_util.hip.
 hipError_t launch_scale_c(const GemmArgs& g, hipStream_t s);
 
 // C = alpha * sum_{s < splits} W_s + beta * C over M x N, the W_s dense M x N
 // partial products (row stride N) at W + s*M*N, summed in ascending s.
-// Defined in kernels_valu.hip.
+// Defined in kernels_util.hip.
 hipError_t launch_splitk_reduce(const float* W, int splits, int M, int N, float alpha, float beta,
                                 float* C, int64_t ldc, hipStream_t s);
 

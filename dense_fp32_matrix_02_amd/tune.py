@@ -74,7 +74,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--shapes", default=",".join(f"{w.M}x{w.N}x{w.K}" for w in workloads.WORKLOADS))
     ap.add_argument("--grid", action="store_true",
-                    help="also measure the grid M, N in {512..8192} (powers of two) x K in {512, 2048, 8192}")
+                    help="also measure the grid M, N in {128..8192} (powers of two) x K in {256, 1024, 4096, 16384}")
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kinds", default="mfma", help="mfma, valu or mfma,valu")
@@ -90,8 +90,10 @@ def main(argv=None):
     results = []
     shapes = parse_shapes(args.shapes)
     if args.grid:
-        sides = [512, 1024, 2048, 4096, 8192]
-        shapes += [(m, n, k) for m in sides for n in sides for k in (512, 2048, 8192)
+        # Every M, N in [64, 16384] and K in [128, 32768] lies within a factor
+        # of two of a grid point in each dimension (the table's lookup radius).
+        sides = [128, 256, 512, 1024, 2048, 4096, 8192]
+        shapes += [(m, n, k) for m in sides for n in sides for k in (256, 1024, 4096, 16384)
                    if (m, n, k) not in shapes]
     for (M, N, K) in shapes:
         A, B = workloads.draw(M, N, K, 1234, "uniform")

@@ -189,9 +189,11 @@ int sgemm_mi355_splitk_with_config(int opA, int opB, int M, int N, int K, float 
 
 /*
  * Split count and tile configuration the library suggests for a problem
- * (host only): no split while the tile grid alone gives at least two
- * workgroups per compute unit, else the smallest power of two that does,
- * with chunks of at least 256 values of k. Writes *splits and *config.
+ * (host only): no split while the unsplit tile grid gives at least two
+ * workgroups per compute unit; otherwise the largest power of two that keeps
+ * chunks of at least 1024 values of k (so K < 2048 is never split). Writes
+ * *splits and *config (the configuration of the chunk products, or of the
+ * whole product when *splits is 1).
  */
 int sgemm_mi355_select_splitk(int opA, int opB, int M, int N, int K, int *splits, int *config);
 

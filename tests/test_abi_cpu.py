@@ -116,6 +116,10 @@ def test_config_metadata():
         if name.startswith("valu"):
             tm = int(name[4:name.index("x")])
             assert threads == (bm // tm) * (bn // 8)
+        else:
+            w = re.search(r"_w(\d+)x(\d+)", name)
+            kg = re.search(r"_kg(\d+)", name)
+            assert threads == 64 * int(w[1]) * int(w[2]) * (int(kg[1]) if kg else 1)
     assert sg.sgemm_mi355_version().count(".") == 2
 
 
@@ -276,7 +280,11 @@ def test_select_splitk():
         assert sp == 1 and sg.sgemm_mi355_config_ops(cid) == (opA, opB)
         sp, cid = sg.sgemm_mi355_select_splitk(opA, opB, 256, 256, 8192)
         assert sp > 1 and sg.sgemm_mi355_config_ops(cid) == (opA, opB)
-    sp, _ = sg.sgemm_mi355_select_splitk(0, 0, 256, 256, 300)
-    assert sp == 1                                    # chunks would be shorter than 256
+    sp, _ = sg.sgemm_mi355_select_splitk(0, 0, 256, 256, 2047)
+    assert sp == 1                                    # chunks would be shorter than 1024
+    sp, _ = sg.sgemm_mi355_select_splitk(0, 0, 64, 64, 65536)
+    assert sp == 64                                   # K / 1024 chunks
+    sp, _ = sg.sgemm_mi355_select_splitk(0, 0, 1024, 1024, 1024)
+    assert sp == 1
     with pytest.raises(sg.SgemmError):
         sg.sgemm_mi355_select_splitk(2, 0, 1, 1, 1)
