@@ -77,8 +77,10 @@ struct Operand {
   static constexpr int TPL = (L == KC) ? BK / 4 : (L == MC ? ROWS / 4 : ROWS);  // threads per line
   static constexpr int LPP = NT / TPL;                                          // lines per pass
   static constexpr int LINES = (L == KC) ? ROWS : (L == MC ? BK : BK / 4);
-  static constexpr int PASSES = LINES / LPP;
-  static_assert(NT % TPL == 0 && LPP >= 1 && LINES % LPP == 0 && PASSES >= 1, "operand load shape");
+  static constexpr int PASSES = (LINES + LPP - 1) / LPP;
+  // When the threads do not divide the lines evenly, the last pass is partial.
+  static constexpr bool PARTIAL = (LINES % LPP) != 0;
+  static_assert(NT % TPL == 0 && LPP >= 1 && PASSES >= 1, "operand load shape");
   static_assert(ROWS % 32 == 0 && BK % 8 == 0, "operand tile shape");
 
   const float* src[PASSES];
@@ -97,7 +99,8 @@ struct Operand {
     valid = R - (r0 + 4 * col);
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      const int line = line0 + p * LPP;
+      int line = line0 + p * LPP;
+      if (PARTIAL && line >= LINES) line = LINES - 1;  // unused slot of a partial pass
       if constexpr (L == KC) {
         int row = r0 + line;
         row = row < R ? row : R - 1;
@@ -119,6 +122,7 @@ struct Operand {
     for (int p = 0; p < PASSES; ++p) {
       const float* s = src[p] + koff;
       const int line = line0 + p * LPP;
+      if (PARTIAL && p == PASSES - 1 && line >= LINES) break;
       if constexpr (L == KC) {
         const int kc = k0 + 4 * col;
         if (!TAIL || kc + 3 < K) {
@@ -149,6 +153,7 @@ struct Operand {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int line = line0 + p * LPP;
+      if (PARTIAL && p == PASSES - 1 && line >= LINES) break;
       float* d = (L == KM) ? lds + col * S + 4 * line : lds + line * S + 4 * col;
       *reinterpret_cast<f32x4*>(d) = reg[p];
     }
@@ -437,6 +442,12 @@ KernelConfig kMfmaConfigs[] = {
     SGEMM_MFMA_KG(32, 32, 256, 1, 1, 16),
     SGEMM_MFMA_KG(64, 64, 128, 2, 2, 4),
     SGEMM_MFMA_KG(128, 64, 64, 2, 2, 4),
+    // 192-row tiles: one tile per compute unit for M near 3000-3072
+    SGEMM_MFMA_N(192, 128, 16, 3, 2),
+    SGEMM_MFMA_KG(192, 128, 16, 3, 2, 2),
+    SGEMM_MFMA_KG(192, 128, 32, 3, 2, 2),
+    SGEMM_MFMA_KG(128, 192, 16, 2, 3, 2),
+    SGEMM_MFMA_N(192, 64, 16, 3, 2),
     // transposed operands (op(A) = A^T and/or op(B) = B^T)
     SGEMM_MFMA_OPS(256, 128, 16, 4, 2),
     SGEMM_MFMA_OPS(128, 64, 16, 2, 2),
