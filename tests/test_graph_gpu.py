@@ -1,0 +1,120 @@
+"""The entry points under HIP graph capture: every launch the library makes
+(the GEMM kernels, the split-K reduction, the C = beta*C kernel for K == 0)
+is an ordinary kernel node, with no memset node, so a captured call can be
+replayed. Each case captures one call, then replays it several times with
+unrelated eager work and synchronisations between the replays, refilling C
+before each replay, and checks every replay against the oracle exactly
+(integer-valued inputs)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import dense_fp32_matrix_02_amd as sg
+import oracle
+import workloads
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    G.require_gpu()
+
+
+def _ints(rows, cols, seed):
+    return workloads.as_numpy(workloads.draw(rows, 1, cols, seed, "int4")[0])
+
+
+def _eager_noise(seed):
+    """Unrelated eager work between replays: another product on other data."""
+    A, B = workloads.draw(300, 200, 100, seed, "int4")
+    C = sg.matmul(A.to("cuda"), B.to("cuda"))
+    torch.cuda.synchronize()
+    G.check_exact(C.cpu().numpy(), workloads.as_numpy(A), workloads.as_numpy(B))
+
+
+def _capture(fn):
+    """Capture fn() into a graph after one eager warm-up call on a side stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    torch.cuda.synchronize()
+    return graph
+
+
+def _replay_and_check(graph, C, C_init, want, label):
+    for r in range(REPLAYS):
+        print(f"[gpu] graph {label} replay {r}", flush=True)
+        C.copy_(C_init)  # eager refill, outside the graph
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(C.cpu().numpy(), want, err_msg=f"{label}, replay {r}")
+        _eager_noise(100 + r)
+
+
+def test_graph_plain_product():
+    M, N, K = 700, 500, 300
+    A, B = _ints(M, K, 1), _ints(K, N, 2)
+    Ad, Bd = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    C = torch.empty((M, N), device="cuda")
+    graph = _capture(lambda: sg.matmul(Ad, Bd, out=C))
+    nan = torch.full((M, N), float("nan"), device="cuda")
+    _replay_and_check(graph, C, nan, oracle.sgemm_f32(A, B), "plain")
+
+
+def test_graph_general_form_reads_c():
+    M, N, K = 257, 333, 129
+    A, B, C0 = _ints(K, M, 3), _ints(K, N, 4), _ints(M, N, 5)  # op(A) = A^T
+    Ad, Bd = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    C0d = torch.from_numpy(C0).cuda()
+    C = C0d.clone()
+    graph = _capture(lambda: sg.gemm(Ad, Bd, C, opA=1, alpha=2.0, beta=-1.0))
+    want = C0.copy()
+    oracle.sgemm_ex_f32(1, 0, 2.0, A, B, -1.0, want)
+    _replay_and_check(graph, C, C0d, want, "general")
+
+
+def test_graph_splitk_two_kernels():
+    M, N, K = 96, 80, 4100
+    A, B = _ints(M, K, 6), _ints(K, N, 7)
+    Ad, Bd = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    C = torch.empty((M, N), device="cuda")
+    splits = 4
+    need = sg.sgemm_mi355_splitk_workspace_size(M, N, K, splits)
+    ws = torch.empty((need + 3) // 4, device="cuda")
+    graph = _capture(lambda: sg.gemm_splitk(Ad, Bd, C, splits=splits, workspace=ws))
+    nan = torch.full((M, N), float("nan"), device="cuda")
+    _replay_and_check(graph, C, nan, oracle.sgemm_f32(A, B), "split-K")
+
+
+def test_graph_k_zero_fills_c():
+    M, N = 130, 77
+    Ad = torch.empty((M, 0), device="cuda")
+    Bd = torch.empty((0, N), device="cuda")
+    C = torch.empty((M, N), device="cuda")
+    graph = _capture(lambda: sg.gemm(Ad, Bd, C))
+    nan = torch.full((M, N), float("nan"), device="cuda")
+    _replay_and_check(graph, C, nan, np.zeros((M, N), np.float32), "K=0")
+
+
+def test_graph_strided_batch():
+    batch, M, N, K = 6, 70, 90, 50
+    A = np.stack([_ints(M, K, 10 + b) for b in range(batch)])
+    B = np.stack([_ints(K, N, 30 + b) for b in range(batch)])
+    Ad, Bd = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    C = torch.empty((batch, M, N), device="cuda")
+    graph = _capture(lambda: sg.gemm_strided_batched(Ad, Bd, C))
+    nan = torch.full((batch, M, N), float("nan"), device="cuda")
+    want = np.stack([oracle.sgemm_f32(A[b], B[b]) for b in range(batch)])
+    _replay_and_check(graph, C, nan, want, "batched")
