@@ -484,6 +484,6 @@ const char* sgemm_mi355_strerror(int code) {
   }
 }
 
-const char* sgemm_mi355_version(void) { return "0.3.0"; }
+const char* sgemm_mi355_version(void) { return "0.4.0"; }
 
 }  // extern "C"
