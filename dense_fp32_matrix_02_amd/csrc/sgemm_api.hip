@@ -26,15 +26,22 @@ constexpr int kCompute = 256;  // compute units on MI355X
 
 // Block tiles the selection rule considers when the table has no entry,
 // largest first, each with the fewest workgroups (counting batch entries) it
-// needs to be chosen. Below the last threshold, a 32x32 tile with its slabs
-// split among wave groups keeps the SIMDs busy; long K takes the deeper one.
-// Thresholds were fitted to the measured grid the table comes from (about 2%
-// slower than the best configuration there, geometric mean).
+// needs to be chosen; a tile is also skipped when the matrix would fill less
+// than kRuleMinFill of its padded tile grid (a batch of 64x64 products in
+// 256x128 tiles computes 8 times the useful work). Below the last threshold,
+// a 32x32 tile with its slabs split among wave groups keeps the SIMDs busy;
+// long K takes the deeper one. Thresholds were fitted to the measured grid
+// the table comes from (about 2% slower than the best configuration there,
+// geometric mean) and to strided batches of 64^3 to 1024^3 products.
 struct RuleTile {
   const char* tile;
   int min_wgs;
 };
-const RuleTile kRuleTiles[] = {{"256x128x16_w4x2", 256}, {"128x64x16_w2x2", 768}, {"64x64x64_w2x2_kg2", 256}};
+const RuleTile kRuleTiles[] = {{"256x128x16_w4x2", 256},
+                               {"128x64x16_w2x2", 768},
+                               {"64x64x32_w2x2", 1024},  // plain products only
+                               {"64x64x64_w2x2_kg2", 256}};
+constexpr double kRuleMinFill = 0.75;
 const char* const kRuleSmall = "32x32x128_w1x1_kg4";
 const char* const kRuleSmallLongK = "32x32x256_w1x1_kg16";
 constexpr int kRuleLongK = 4096;
@@ -71,7 +78,11 @@ int rule_select(int opA, int opB, int M, int N, int K, int batch) {
   for (const RuleTile& r : kRuleTiles) {
     std::snprintf(name, sizeof(name), "mfma32_%s%s", r.tile, ops_suffix(opA, opB));
     const int id = config_id(name);
-    if (id >= 0 && tiles_for(*config_at(id), M, N) * gy >= r.min_wgs) return id;
+    if (id < 0) continue;
+    const KernelConfig& c = *config_at(id);
+    const int64_t tiles = tiles_for(c, M, N);
+    const double fill = tiles > 0 ? (double)M * N / ((double)tiles * c.bm * c.bn) : 1.0;
+    if (tiles * gy >= r.min_wgs && fill >= kRuleMinFill) return id;
   }
   std::snprintf(name, sizeof(name), "mfma32_%s%s", K >= kRuleLongK ? kRuleSmallLongK : kRuleSmall,
                 ops_suffix(opA, opB));

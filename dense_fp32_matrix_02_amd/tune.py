@@ -8,9 +8,14 @@ seeded U[-1,1) inputs; the median of `reps` event-timed launches decides.
 
     python -m dense_fp32_matrix_02_amd.tune [--shapes 8192x8192x8192,...]
         [--reps 20] [--json results.json] [--table tile_table.inc]
+        [--ops nn|tn|nt|tt] [--batch B]
 
 ``--table`` writes a tile_table.inc with one exact-shape entry per measured
-shape; copy it to csrc/ and rebuild to use it.
+shape; copy it to csrc/ and rebuild to use it. ``--ops`` times the
+configurations built for transposed operands (op(A) = A^T for a first letter
+t, op(B) = B^T for a second), on operands stored transposed; ``--batch``
+times strided batches of B independent products per launch. The table holds
+plain single products only, so ``--table`` needs the defaults of both.
 """
 from __future__ import annotations
 
@@ -50,20 +55,51 @@ def parse_shapes(text):
     return out
 
 
-def time_config(M, N, K, cid, reps, warmup, A, B, C):
+def time_call(call, reps, warmup):
+    """Median of `reps` event-timed calls after `warmup` untimed ones (ms)."""
     import torch
-    import dense_fp32_matrix_02_amd as sg
 
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        sg.matmul(A, B, out=C, config=cid, stream=stream)
+        call(stream)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for s, e in ev:
         s.record(stream)
-        sg.matmul(A, B, out=C, config=cid, stream=stream)
+        call(stream)
         e.record(stream)
     torch.cuda.synchronize()
     return statistics.median(s.elapsed_time(e) for s, e in ev)
+
+
+def make_inputs(M, N, K, opA, opB, batch):
+    """Device operands for one shape: op(A) is M x K and op(B) is K x N, stored
+    transposed for a T op; with batch > 1, `batch` independent entries."""
+    import torch
+    import workloads
+
+    def one(seed):
+        A, B = workloads.draw(M, N, K, seed, "uniform")
+        A = A.t().contiguous() if opA else A
+        B = B.t().contiguous() if opB else B
+        return A, B
+
+    if batch == 1:
+        A, B = one(1234)
+        return A.to("cuda"), B.to("cuda"), torch.empty((M, N), device="cuda")
+    pairs = [one(1234 + b) for b in range(batch)]
+    A = torch.stack([p[0] for p in pairs]).to("cuda")
+    B = torch.stack([p[1] for p in pairs]).to("cuda")
+    return A, B, torch.empty((batch, M, N), device="cuda")
+
+
+def config_call(A, B, C, cid, opA, opB, batch):
+    import dense_fp32_matrix_02_amd as sg
+
+    if batch == 1 and not opA and not opB:
+        return lambda stream: sg.matmul(A, B, out=C, config=cid, stream=stream)
+    if batch == 1:
+        return lambda stream: sg.gemm(A, B, C, opA=opA, opB=opB, config=cid, stream=stream)
+    return lambda stream: sg.gemm_strided_batched(A, B, C, opA=opA, opB=opB, config=cid, stream=stream)
 
 
 def main(argv=None):
@@ -81,12 +117,19 @@ def main(argv=None):
     ap.add_argument("--splitk", default="", help="split counts to time with sgemm_mi355_splitk, e.g. 2,4,8")
     ap.add_argument("--json", default=None)
     ap.add_argument("--table", default=None)
+    ap.add_argument("--ops", default="nn", choices=["nn", "tn", "nt", "tt"])
+    ap.add_argument("--batch", type=int, default=1)
     args = ap.parse_args(argv)
+    opA, opB = int(args.ops[0] == "t"), int(args.ops[1] == "t")
+    if args.table and (opA or opB or args.batch != 1):
+        ap.error("--table records plain single products: leave --ops and --batch at their defaults")
+    if args.splitk and (opA or opB or args.batch != 1):
+        ap.error("--splitk times plain single products")
 
     names = sg.config_names()
     kinds = args.kinds.split(",")
     cands = [i for i, n in enumerate(names)
-             if n.startswith(tuple(kinds)) and sg.sgemm_mi355_config_ops(i) == (0, 0)]
+             if n.startswith(tuple(kinds)) and sg.sgemm_mi355_config_ops(i) == (opA, opB)]
     results = []
     shapes = parse_shapes(args.shapes)
     if args.grid:
@@ -95,38 +138,28 @@ def main(argv=None):
         sides = [128, 256, 512, 1024, 2048, 4096, 8192]
         shapes += [(m, n, k) for m in sides for n in sides for k in (256, 1024, 4096, 16384)
                    if (m, n, k) not in shapes]
+    tag = ("" if args.ops == "nn" else f" {args.ops}") + ("" if args.batch == 1 else f" x{args.batch}")
     for (M, N, K) in shapes:
-        A, B = workloads.draw(M, N, K, 1234, "uniform")
-        Ad, Bd = A.to("cuda"), B.to("cuda")
-        C = torch.empty((M, N), device="cuda")
-        row = {"M": M, "N": N, "K": K, "times_ms": {}}
+        Ad, Bd, C = make_inputs(M, N, K, opA, opB, args.batch)
+        row = {"M": M, "N": N, "K": K, "ops": args.ops, "batch": args.batch, "times_ms": {}}
+        flops = 2 * M * N * K * args.batch
         for cid in cands:
-            ms = time_config(M, N, K, cid, args.reps, args.warmup, Ad, Bd, C)
+            ms = time_call(config_call(Ad, Bd, C, cid, opA, opB, args.batch), args.reps, args.warmup)
             row["times_ms"][names[cid]] = ms
-            print(f"{M}x{N}x{K} {names[cid]:28s} {ms:9.4f} ms {2 * M * N * K / ms / 1e9:9.2f} TFLOP/s",
+            print(f"{M}x{N}x{K}{tag} {names[cid]:28s} {ms:9.4f} ms {flops / ms / 1e9:9.2f} TFLOP/s",
                   flush=True)
         for sp in [int(x) for x in args.splitk.split(",") if x]:
             need = sg.sgemm_mi355_splitk_workspace_size(M, N, K, sp)
             ws = torch.empty((need + 3) // 4 + 1, device="cuda")
-            stream = torch.cuda.current_stream()
-            run = lambda: sg.gemm_splitk(Ad, Bd, C, splits=sp, workspace=ws, stream=stream)
-            for _ in range(args.warmup):
-                run()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(args.reps)]
-            for s0, e0 in ev:
-                s0.record(stream)
-                run()
-                e0.record(stream)
-            torch.cuda.synchronize()
-            ms = statistics.median(s0.elapsed_time(e0) for s0, e0 in ev)
+            ms = time_call(lambda stream: sg.gemm_splitk(Ad, Bd, C, splits=sp, workspace=ws, stream=stream),
+                           args.reps, args.warmup)
             row.setdefault("splitk_ms", {})[sp] = ms
             print(f"{M}x{N}x{K} splitk={sp:<3d} (gemm + reduce)        {ms:9.4f} ms "
                   f"{2 * M * N * K / ms / 1e9:9.2f} TFLOP/s", flush=True)
         mfma = {n: t for n, t in row["times_ms"].items() if n.startswith("mfma")}
         if mfma:
             row["best"] = min(mfma, key=mfma.get)
-            row["default"] = names[sg.sgemm_mi355_select_config(M, N, K)]
+            row["default"] = names[sg.sgemm_mi355_select_config_ex(opA, opB, M, N, K, args.batch)]
             print(f"  best {row['best']}  (table/rule picks {row['default']})", flush=True)
         results.append(row)
         del Ad, Bd, C
