@@ -413,6 +413,10 @@ KernelConfig kMfmaConfigs[] = {
     SGEMM_MFMA_N(256, 128, 16, 4, 2),
     SGEMM_MFMA_N(256, 128, 32, 4, 2),
     SGEMM_MFMA_G8(256, 128, 16, 4, 2),
+    // B staged k-major with 16 waves: 128-bit fragment reads for both operands
+    SGEMM_MFMA_K(256, 256, 16, 4, 4),
+    SGEMM_MFMA_K(256, 128, 16, 4, 2),
+    SGEMM_MFMA_K(256, 128, 32, 4, 2),
     // medium tiles: grid fill on mid-sized and ragged problems
     SGEMM_MFMA_N(128, 128, 16, 2, 2),
     SGEMM_MFMA_N(128, 128, 32, 2, 2),
@@ -451,6 +455,19 @@ KernelConfig kMfmaConfigs[] = {
     // transposed operands (op(A) = A^T and/or op(B) = B^T)
     SGEMM_MFMA_OPS(256, 128, 16, 4, 2),
     SGEMM_MFMA_OPS(128, 64, 16, 2, 2),
+    // more layouts for the transposed forms: _ak stages op(A) = A^T k-major
+    // (b128 fragment reads), 32-deep slabs read whole 128-byte lines of a
+    // k-contiguous operand, and 256x256 tiles halve the panel re-reads
+    SGEMM_MFMA_CFG(256, 128, 16, 4, 2, 1, 4, KM, MC, 1, 0, "_ak_tn"),
+    SGEMM_MFMA_CFG(256, 256, 16, 4, 4, 1, 4, MC, MC, 1, 0, "_tn"),
+    SGEMM_MFMA_CFG(256, 256, 16, 4, 4, 1, 4, KM, MC, 1, 0, "_ak_tn"),
+    SGEMM_MFMA_CFG(256, 128, 32, 4, 2, 1, 4, KC, KC, 0, 1, "_nt"),
+    SGEMM_MFMA_CFG(256, 256, 16, 4, 4, 1, 4, KC, KC, 0, 1, "_nt"),
+    SGEMM_MFMA_CFG(256, 256, 32, 4, 4, 1, 4, KC, KC, 0, 1, "_nt"),
+    SGEMM_MFMA_CFG(256, 128, 16, 4, 2, 1, 4, KM, KC, 1, 1, "_ak_tt"),
+    SGEMM_MFMA_CFG(256, 256, 16, 4, 4, 1, 4, MC, KC, 1, 1, "_tt"),
+    SGEMM_MFMA_CFG(256, 256, 16, 4, 4, 1, 4, KM, KC, 1, 1, "_ak_tt"),
+    SGEMM_MFMA_CFG(256, 256, 16, 4, 4, 1, 4, KM, KM, 1, 0, "_ak_bk_tn"),
     SGEMM_MFMA_OPS_KG(64, 64, 64, 2, 2, 2),
     SGEMM_MFMA_OPS_KG(32, 32, 128, 1, 1, 4),
     SGEMM_MFMA_OPS_KG(32, 32, 256, 1, 1, 16),

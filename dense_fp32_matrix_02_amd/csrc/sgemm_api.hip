@@ -24,27 +24,43 @@ struct ShapeEntry {
 
 constexpr int kCompute = 256;  // compute units on MI355X
 
-// Block tiles the selection rule considers when the table has no entry,
-// largest first, each with the fewest workgroups (counting batch entries) it
-// needs to be chosen; a tile is also skipped when the matrix would fill less
-// than kRuleMinFill of its padded tile grid (a batch of 64x64 products in
-// 256x128 tiles computes 8 times the useful work). Below the last threshold,
-// a 32x32 tile with its slabs split among wave groups keeps the SIMDs busy;
-// long K takes the deeper one. Thresholds were fitted to the measured grid
-// the table comes from (about 2% slower than the best configuration there,
-// geometric mean) and to strided batches of 64^3 to 1024^3 products.
+// Block tiles the selection rule considers when the table has no entry, per
+// operand pair (plain, op(A) = A^T, op(B) = B^T, both), largest first, each
+// with the fewest workgroups (counting batch entries) it needs to be chosen;
+// a tile is also skipped when the matrix would fill less than kRuleMinFill of
+// its padded tile grid (a batch of 64x64 products in 256x128 tiles computes 8
+// times the useful work). Below the last threshold, a 32x32 tile with its
+// slabs split among wave groups keeps the SIMDs busy; long K takes the deeper
+// one. The plain thresholds were fitted to the measured grid the table comes
+// from (about 2% slower than the best configuration there, geometric mean)
+// and to strided batches of 64^3 to 1024^3 products; the transposed forms
+// were measured at 2048^3 to 8192^3 and on the ragged workload.
 struct RuleTile {
-  const char* tile;
+  const char* config;
   int min_wgs;
 };
-const RuleTile kRuleTiles[] = {{"256x128x16_w4x2", 256},
-                               {"128x64x16_w2x2", 768},
-                               {"64x64x32_w2x2", 1024},  // plain products only
-                               {"64x64x64_w2x2_kg2", 256}};
-constexpr double kRuleMinFill = 0.75;
+const RuleTile kRulePlain[] = {{"mfma32_256x128x16_w4x2", 256},
+                               {"mfma32_128x64x16_w2x2", 768},
+                               {"mfma32_64x64x32_w2x2", 1024},
+                               {"mfma32_64x64x64_w2x2_kg2", 256}};
+const RuleTile kRuleTN[] = {{"mfma32_256x256x16_w4x4_ak_tn", 256},
+                            {"mfma32_256x128x16_w4x2_tn", 256},
+                            {"mfma32_128x64x16_w2x2_tn", 512},
+                            {"mfma32_64x64x64_w2x2_kg2_tn", 256}};
+const RuleTile kRuleNT[] = {{"mfma32_256x256x32_w4x4_nt", 256},
+                            {"mfma32_256x128x16_w4x2_nt", 256},
+                            {"mfma32_128x64x16_w2x2_nt", 512},
+                            {"mfma32_64x64x64_w2x2_kg2_nt", 256}};
+const RuleTile kRuleTT[] = {{"mfma32_256x256x16_w4x4_tt", 256},
+                            {"mfma32_256x128x16_w4x2_tt", 256},
+                            {"mfma32_128x64x16_w2x2_tt", 512},
+                            {"mfma32_64x64x64_w2x2_kg2_tt", 256}};
+const RuleTile* const kRuleTiles[2][2] = {{kRulePlain, kRuleNT}, {kRuleTN, kRuleTT}};
+constexpr int kRuleTileCount = 4;
 const char* const kRuleSmall = "32x32x128_w1x1_kg4";
 const char* const kRuleSmallLongK = "32x32x256_w1x1_kg16";
 constexpr int kRuleLongK = 4096;
+constexpr double kRuleMinFill = 0.75;
 
 int num_configs() { return kNumMfmaConfigs + kNumValuConfigs; }
 
@@ -74,16 +90,16 @@ const char* ops_suffix(int opA, int opB) {
 // small k-group tile for this K.
 int rule_select(int opA, int opB, int M, int N, int K, int batch) {
   const int64_t gy = batch < kMaxGridY ? batch : kMaxGridY;
-  char name[64];
-  for (const RuleTile& r : kRuleTiles) {
-    std::snprintf(name, sizeof(name), "mfma32_%s%s", r.tile, ops_suffix(opA, opB));
-    const int id = config_id(name);
+  const RuleTile* tiles = kRuleTiles[opA][opB];
+  for (int i = 0; i < kRuleTileCount; ++i) {
+    const int id = config_id(tiles[i].config);
     if (id < 0) continue;
     const KernelConfig& c = *config_at(id);
-    const int64_t tiles = tiles_for(c, M, N);
-    const double fill = tiles > 0 ? (double)M * N / ((double)tiles * c.bm * c.bn) : 1.0;
-    if (tiles * gy >= r.min_wgs && fill >= kRuleMinFill) return id;
+    const int64_t n = tiles_for(c, M, N);
+    const double fill = n > 0 ? (double)M * N / ((double)n * c.bm * c.bn) : 1.0;
+    if (n * gy >= tiles[i].min_wgs && fill >= kRuleMinFill) return id;
   }
+  char name[64];
   std::snprintf(name, sizeof(name), "mfma32_%s%s", K >= kRuleLongK ? kRuleSmallLongK : kRuleSmall,
                 ops_suffix(opA, opB));
   return config_id(name);
