@@ -21,6 +21,7 @@ struct ShapeEntry {
   const char* config;
 };
 #include "tile_table.inc"
+constexpr int kTableEntries = sizeof(kShapeTable) / sizeof(kShapeTable[0]) - 1;  // without the sentinel
 
 constexpr int kCompute = 256;  // compute units on MI355X
 
@@ -86,23 +87,47 @@ const char* ops_suffix(int opA, int opB) {
   return s[opA][opB];
 }
 
+// Configuration names used by the selection, resolved to ids once per
+// process (a function-local static: initialised on first use, thread-safe,
+// never written afterwards), so a call costs no string comparisons.
+struct Resolved {
+  int rule[2][2][kRuleTileCount];  // -1 where a configuration is not built
+  int small[2][2][2];              // [opA][opB][long K]
+  int table[kTableEntries];         // id of each table entry (-1 if unknown)
+};
+
+const Resolved& resolved() {
+  static const Resolved r = [] {
+    Resolved x;
+    for (int a = 0; a < 2; ++a)
+      for (int b = 0; b < 2; ++b) {
+        for (int i = 0; i < kRuleTileCount; ++i) x.rule[a][b][i] = config_id(kRuleTiles[a][b][i].config);
+        for (int l = 0; l < 2; ++l) {
+          char name[64];
+          std::snprintf(name, sizeof(name), "mfma32_%s%s", l ? kRuleSmallLongK : kRuleSmall, ops_suffix(a, b));
+          x.small[a][b][l] = config_id(name);
+        }
+      }
+    for (int t = 0; t < kTableEntries; ++t) x.table[t] = config_id(kShapeTable[t].config);
+    return x;
+  }();
+  return r;
+}
+
 // The first rule tile whose grid reaches its workgroup threshold, else the
 // small k-group tile for this K.
 int rule_select(int opA, int opB, int M, int N, int K, int batch) {
   const int64_t gy = batch < kMaxGridY ? batch : kMaxGridY;
-  const RuleTile* tiles = kRuleTiles[opA][opB];
+  const Resolved& rs = resolved();
   for (int i = 0; i < kRuleTileCount; ++i) {
-    const int id = config_id(tiles[i].config);
+    const int id = rs.rule[opA][opB][i];
     if (id < 0) continue;
     const KernelConfig& c = *config_at(id);
     const int64_t n = tiles_for(c, M, N);
     const double fill = n > 0 ? (double)M * N / ((double)n * c.bm * c.bn) : 1.0;
-    if (n * gy >= tiles[i].min_wgs && fill >= kRuleMinFill) return id;
+    if (n * gy >= kRuleTiles[opA][opB][i].min_wgs && fill >= kRuleMinFill) return id;
   }
-  char name[64];
-  std::snprintf(name, sizeof(name), "mfma32_%s%s", K >= kRuleLongK ? kRuleSmallLongK : kRuleSmall,
-                ops_suffix(opA, opB));
-  return config_id(name);
+  return rs.small[opA][opB][K >= kRuleLongK ? 1 : 0];
 }
 
 // Table lookup for the plain product: the measured entry of the same shape,
@@ -110,12 +135,18 @@ int rule_select(int opA, int opB, int M, int N, int K, int batch) {
 // within a factor of two in each dimension; -1 when none qualifies.
 int table_select(int M, int N, int K) {
   if (M <= 0 || N <= 0 || K <= 0) return -1;
+  const int* ids = resolved().table;
   int best = -1;
   double best_d = 1e30;
-  for (const ShapeEntry* e = kShapeTable; e->config; ++e) {
-    const int id = config_id(e->config);
+  for (int t = 0; t < kTableEntries; ++t) {
+    const ShapeEntry* e = &kShapeTable[t];
+    const int id = ids[t];
     if (id < 0) continue;
     if (e->M == M && e->N == N && e->K == K) return id;
+    // within a factor of two in every dimension (integer test before any log)
+    if ((int64_t)M > 2LL * e->M || (int64_t)e->M > 2LL * M || (int64_t)N > 2LL * e->N ||
+        (int64_t)e->N > 2LL * N || (int64_t)K > 2LL * e->K || (int64_t)e->K > 2LL * K)
+      continue;
     const double dm = std::fabs(std::log2((double)M / e->M));
     const double dn = std::fabs(std::log2((double)N / e->N));
     const double dk = std::fabs(std::log2((double)K / e->K));
@@ -143,9 +174,9 @@ int select_mfma(int opA, int opB, int M, int N, int K, int batch) {
 const char* const kValuRuleTiles[] = {"valu8x8_128x128x8", "valu8x8_64x64x16"};
 
 int select_valu(int M, int N) {
+  static const int ids[2] = {config_id(kValuRuleTiles[0]), config_id(kValuRuleTiles[1])};
   int last = -1;
-  for (const char* name : kValuRuleTiles) {
-    const int id = config_id(name);
+  for (const int id : ids) {
     if (id < 0) continue;
     last = id;
     if (tiles_for(*config_at(id), M, N) >= kCompute) return id;

@@ -288,3 +288,45 @@ def test_select_splitk():
     assert sp == 1
     with pytest.raises(sg.SgemmError):
         sg.sgemm_mi355_select_splitk(2, 0, 1, 1, 1)
+
+
+def _table_entries():
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "dense_fp32_matrix_02_amd", "csrc", "tile_table.inc")
+    rows = re.findall(r'\{(\d+), (\d+), (\d+), "([^"]+)"\}', open(path).read())
+    return [(int(m), int(n), int(k), name) for m, n, k, name in rows]
+
+
+def test_table_lookup_matches_its_definition():
+    """The plain product's table lookup, written out here from its definition:
+    the entry of the same shape, else the nearest entry in log2 distance
+    among those within a factor of two in every dimension (first one on a
+    tie), else the rule (not covered here)."""
+    import math
+    import random
+
+    entries = _table_entries()
+    names = sg.config_names()
+    rng = random.Random(7)
+    shapes = [(m, n, k) for m, n, k, _ in entries[:20]]
+    shapes += [(rng.randint(40, 20000), rng.randint(40, 20000), rng.randint(60, 40000)) for _ in range(400)]
+    checked = 0
+    for M, N, K in shapes:
+        want = None
+        exact = [name for m, n, k, name in entries if (m, n, k) == (M, N, K)]
+        if exact:
+            want = exact[0]
+        else:
+            best = None
+            for m, n, k, name in entries:
+                d = [abs(math.log2(M / m)), abs(math.log2(N / n)), abs(math.log2(K / k))]
+                if max(d) > 1.0:
+                    continue
+                if best is None or sum(d) < best[0]:
+                    best = (sum(d), name)
+            want = best[1] if best else None
+        if want is None:
+            continue
+        assert names[sg.sgemm_mi355_select_config(M, N, K)] == want, (M, N, K)
+        checked += 1
+    assert checked > 100
