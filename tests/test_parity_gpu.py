@@ -237,3 +237,22 @@ def test_runs_on_a_side_stream():
         sg.matmul(Ad, Bd, out=out, stream=s)
     s.synchronize()
     G.check_exact(out.cpu().numpy(), np_(A), np_(B))
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_very_long_k_exact(kind):
+    """K of about a million with a tiny ragged M x N: tens of thousands of
+    slabs in one workgroup (k-group tiles on the matrix-core path), and the
+    same product as 64 split-K chunks. Integer inputs in {-4..4} keep every
+    partial sum below 2^24, so both are exact."""
+    M, N, K = 33, 47, 1_000_003
+    A, B = workloads.draw(M, N, K, 91, "int4")
+    An, Bn = np_(A), np_(B)
+    want = oracle.sgemm_f32(An, Bn)
+    C = G.gemm(A, B, kind=kind)
+    np.testing.assert_array_equal(C, want)
+    if kind == "mfma":
+        print(f"[gpu] split-K 64 chunks M={M} N={N} K={K}", flush=True)
+        Cs = sg.gemm_splitk(G.dev(A), G.dev(B), splits=64)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(Cs.cpu().numpy(), want)
