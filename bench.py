@@ -35,22 +35,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = {"mfma": ("kernels_mfma.hip", "sgemm_internal.h"),
-                  "valu": ("kernels_valu.hip", "sgemm_internal.h")}
+def kernel_sources(config_name: str):
+    """The source files that define a configuration's kernel."""
+    if config_name.startswith("valu"):
+        return ("kernels_valu.hip", "sgemm_internal.h")
+    if "_lds" in config_name:
+        return ("kernels_mfma_dma.hip", "sgemm_internal.h")
+    return ("kernels_mfma.hip", "sgemm_internal.h")
 
 
-def kernel_source_hash(kind: str = "mfma") -> str:
-    """Hash of the source files that define the kind's GEMM kernels: counter
+def kernel_source_hash(config_name: str) -> str:
+    """Hash of the source files that define the configuration's kernel: counter
     figures taken on other sources no longer describe the kernel."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_fp32_matrix_02_amd", "csrc")
-    for name in KERNEL_SOURCES[kind]:
+    for name in kernel_sources(config_name):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, config_name: str, kind: str = "mfma"):
+def stored_traffic(workload: str, config_name: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -59,7 +64,7 @@ def stored_traffic(workload: str, config_name: str, kind: str = "mfma"):
     with open(path) as f:
         table = json.load(f)
     e = table.get(f"{workload}/{config_name}")
-    if not e or e.get("kernel_source_hash") != kernel_source_hash(kind):
+    if not e or e.get("kernel_source_hash") != kernel_source_hash(config_name):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -221,7 +226,7 @@ def main():
                      "frac_fp32_mfma_peak": round(va / (PEAK_MFMA_TFLOPS * 1e3), 4)})
         log(f"[bench] also {wa.name}: {va:.1f} GFLOP/s ({ra['config_name']})")
 
-    traffic = stored_traffic(w.name, r["config_name"], args.kind)
+    traffic = stored_traffic(w.name, r["config_name"])
     out = {
         "metric": "SGEMM GFLOP/s (FP32) at N=4096/8192; % of MI355X FP32 peak",
         "value": round(value, 1),

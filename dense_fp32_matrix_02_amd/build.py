@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsgemm_mi355.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["kernels_mfma.hip", "kernels_valu.hip", "kernels_util.hip", "sgemm_api.hip"]
+SOURCES = ["kernels_mfma.hip", "kernels_mfma_dma.hip", "kernels_valu.hip", "kernels_util.hip", "sgemm_api.hip"]
 ARCH = os.environ.get("SGEMM_MI355_ARCH", "gfx950")
 
 HIPFLAGS = [

@@ -41,9 +41,11 @@ struct KernelConfig {
 };
 
 // Host-only tables (not const: a const global would also be emitted for the
-// device). Defined in kernels_mfma.hip and kernels_valu.hip.
+// device). Defined in kernels_mfma.hip, kernels_mfma_dma.hip and kernels_valu.hip.
 extern KernelConfig kMfmaConfigs[];
 extern const int kNumMfmaConfigs;
+extern KernelConfig kMfmaDmaConfigs[];  // defined in kernels_mfma_dma.hip
+extern const int kNumMfmaDmaConfigs;
 extern KernelConfig kValuConfigs[];
 extern const int kNumValuConfigs;
 

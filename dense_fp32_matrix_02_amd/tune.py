@@ -35,9 +35,11 @@ TABLE_HEADER = """\
 // uses. The best tile is an empirical question (CUDA Handbook section 17.3:
 // the microtile is chosen by sweeping; GPU Parallel Book section 9.6: the
 // occupancy setting is found by measurement), so each entry records the
-// fastest configuration measured on MI355X for one shape. A shape without
-// its own entry takes the nearest measured shape (in log M, log N, log K,
-// within a factor of two in each), else the rule in sgemm_api.hip.
+// fastest register-staged configuration measured on MI355X for one shape
+// (the direct-to-LDS kernel is chosen by rule on top, for problems that
+// qualify). A shape without its own entry takes the nearest measured shape
+// (in log M, log N, log K, within a factor of two in each), else the rule in
+// sgemm_api.hip.
 //
 // Written by dense_fp32_matrix_02_amd/tune.py (median of {reps} launches per
 // configuration). Format: {{M, N, K, "configuration name"}}.
@@ -117,6 +119,8 @@ def main(argv=None):
     ap.add_argument("--splitk", default="", help="split counts to time with sgemm_mi355_splitk, e.g. 2,4,8")
     ap.add_argument("--json", default=None)
     ap.add_argument("--table", default=None)
+    ap.add_argument("--from-json", default=None, metavar="JSON",
+                    help="write --table from a saved --json result instead of measuring")
     ap.add_argument("--ops", default="nn", choices=["nn", "tn", "nt", "tt"])
     ap.add_argument("--batch", type=int, default=1)
     args = ap.parse_args(argv)
@@ -125,6 +129,11 @@ def main(argv=None):
         ap.error("--table records plain single products: leave --ops and --batch at their defaults")
     if args.splitk and (opA or opB or args.batch != 1):
         ap.error("--splitk times plain single products")
+
+    if args.from_json:
+        with open(args.from_json) as f:
+            write_table(json.load(f), args.table, args.reps)
+        return
 
     names = sg.config_names()
     kinds = args.kinds.split(",")
@@ -167,12 +176,21 @@ def main(argv=None):
         with open(args.json, "w") as f:
             json.dump(results, f, indent=1)
     if args.table:
-        with open(args.table, "w") as f:
-            f.write(TABLE_HEADER.format(reps=args.reps))
-            for r in results:
-                if "best" in r:
-                    f.write(f'    {{{r["M"]}, {r["N"]}, {r["K"]}, "{r["best"]}"}},\n')
-            f.write("    {0, 0, 0, nullptr},  // sentinel\n};\n")
+        write_table(results, args.table, args.reps)
+
+
+def write_table(results, path, reps):
+    """One entry per measured shape: the fastest register-staged configuration.
+    Direct-to-LDS configurations (_lds) are left out: the library switches to
+    them by rule, only for problems that qualify for direct loads, so a
+    nearest-shape lookup never lands on one for a problem that does not."""
+    with open(path, "w") as f:
+        f.write(TABLE_HEADER.format(reps=reps))
+        for r in results:
+            t = {n: ms for n, ms in r["times_ms"].items() if n.startswith("mfma") and "_lds" not in n}
+            if t:
+                f.write(f'    {{{r["M"]}, {r["N"]}, {r["K"]}, "{min(t, key=t.get)}"}},\n')
+        f.write("    {0, 0, 0, nullptr},  // sentinel\n};\n")
 
 
 if __name__ == "__main__":

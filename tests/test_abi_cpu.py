@@ -327,6 +327,40 @@ def test_table_lookup_matches_its_definition():
             want = best[1] if best else None
         if want is None:
             continue
+        if _direct_qualifies(M, N, K):
+            want = "mfma32_256x256x16_w4x4_lds2"
         assert names[sg.sgemm_mi355_select_config(M, N, K)] == want, (M, N, K)
         checked += 1
     assert checked > 100
+
+
+def _direct_qualifies(M, N, K, batch=1):
+    """The switch to the direct-to-LDS 256x256x16 kernel, from its definition:
+    N a multiple of 256 and K of 16 (aligned operands assumed), at least 256
+    workgroups, at least 75% of the padded tile grid useful and at least 90%
+    of the last wave of 256 workgroups occupied."""
+    import math
+    if M <= 0 or K <= 0 or N % 256 or K % 16:
+        return False
+    tiles = math.ceil(M / 256) * (N // 256)
+    wgs = tiles * min(batch, 65535)
+    fill = M * N / (tiles * 256 * 256)
+    wave = wgs / (math.ceil(wgs / 256) * 256)
+    return wgs >= 256 and fill >= 0.75 and wave >= 0.9
+
+
+def test_direct_kernel_switch_matches_its_definition():
+    import random
+    rng = random.Random(11)
+    names = sg.config_names()
+    shapes = [(8192, 8192, 8192), (4096, 4096, 4096), (6144, 6144, 6144), (8000, 8000, 8000),
+              (4096, 4096, 4100), (1024, 8192, 1024), (300, 65536, 64)]
+    shapes += [(rng.randint(1, 12000), 256 * rng.randint(1, 48), 16 * rng.randint(1, 600)) for _ in range(300)]
+    for M, N, K in shapes:
+        got = names[sg.sgemm_mi355_select_config(M, N, K)]
+        assert (got == "mfma32_256x256x16_w4x4_lds2") == _direct_qualifies(M, N, K), (M, N, K, got)
+        for opA, opB in [(1, 0), (0, 1), (1, 1)]:  # the direct kernel is plain-only
+            assert "_lds" not in names[sg.sgemm_mi355_select_config_ex(opA, opB, M, N, K, 1)]
+    for M, N, K, batch in [(1024, 1024, 1024, 64), (512, 512, 64, 1000), (100, 256, 16, 3)]:
+        got = names[sg.sgemm_mi355_select_config_ex(0, 0, M, N, K, batch)]
+        assert (got == "mfma32_256x256x16_w4x4_lds2") == _direct_qualifies(M, N, K, batch), (M, N, K, batch)

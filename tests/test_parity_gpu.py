@@ -256,3 +256,39 @@ def test_very_long_k_exact(kind):
         Cs = sg.gemm_splitk(G.dev(A), G.dev(B), splits=64)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(Cs.cpu().numpy(), want)
+
+
+DIRECT_IDS = [i for i, n in enumerate(CONFIG_NAMES) if "_lds" in n]
+
+
+@pytest.mark.parametrize("cid", DIRECT_IDS, ids=[CONFIG_NAMES[i] for i in DIRECT_IDS])
+def test_direct_lds_configs_exact(cid):
+    """Configurations that stage slabs with direct global-to-LDS loads take
+    that path only for 16-byte aligned operands with N a multiple of the tile
+    width and K a multiple of the slab depth: exercise it with ragged M and
+    slab counts that leave every remainder of the stage count, then a batch
+    and a split-K chunking, all exact on integer inputs."""
+    bm, bn, bk, _ = sg.sgemm_mi355_config_info(cid)
+    seed = 500
+    for M in (1, bm - 1, bm + 3, 2 * bm):
+        for slabs in (1, 2, 3, 7, 32):
+            seed += 1
+            A, B = workloads.draw(M, 2 * bn, slabs * bk, seed, "int4")
+            C = _run_config(A, B, cid)
+            G.check_exact(C, np_(A), np_(B))
+    # strided batch of 3 entries (16-byte aligned strides)
+    batch, M, N, K = 3, bm + 5, bn, 9 * bk
+    A = torch.stack([workloads.draw(M, N, K, 700 + b, "int4")[0] for b in range(batch)])
+    B = torch.stack([workloads.draw(M, N, K, 800 + b, "int4")[1] for b in range(batch)])
+    print(f"[gpu] config={CONFIG_NAMES[cid]} batch={batch} M={M} N={N} K={K}", flush=True)
+    C = sg.gemm_strided_batched(G.dev(A), G.dev(B), config=cid)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        np.testing.assert_array_equal(C[b].cpu().numpy(), oracle.sgemm_f32(np_(A[b]), np_(B[b])))
+    # split-K: chunks of 32 slabs, the last one short but whole slabs
+    M, N, K = bm - 7, bn, 70 * bk
+    A, B = workloads.draw(M, N, K, 900, "int4")
+    print(f"[gpu] config={CONFIG_NAMES[cid]} split-K M={M} N={N} K={K}", flush=True)
+    Cs = sg.gemm_splitk(G.dev(A), G.dev(B), splits=3, config=cid)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(Cs.cpu().numpy(), oracle.sgemm_f32(np_(A), np_(B)))
