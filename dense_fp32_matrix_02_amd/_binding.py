@@ -65,6 +65,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sgemm_mi355_select_config_ex.argtypes = [_I] * 6
     lib.sgemm_mi355_select_config_valu.argtypes = [_I] * 3
     lib.sgemm_mi355_config_ops.argtypes = [_I, ctypes.POINTER(_I), ctypes.POINTER(_I)]
+    lib.sgemm_mi355_config_occupancy.argtypes = [_I, ctypes.POINTER(_I)]
     lib.sgemm_mi355_select_config.argtypes = [_I, _I, _I]
     lib.sgemm_mi355_num_configs.argtypes = []
     lib.sgemm_mi355_config_name.argtypes = [_I]
@@ -165,6 +166,16 @@ def sgemm_mi355_config_ops(config):
     if rc != OK:
         raise SgemmError(rc, "sgemm_mi355_config_ops")
     return a.value, b.value
+
+
+def sgemm_mi355_config_occupancy(config) -> int:
+    """Workgroups of the configuration one compute unit holds at once (needs
+    a GPU), or raise SgemmError."""
+    n = _I()
+    rc = load().sgemm_mi355_config_occupancy(config, ctypes.byref(n))
+    if rc != OK:
+        raise SgemmError(rc, "sgemm_mi355_config_occupancy")
+    return n.value
 
 
 def sgemm_mi355_validate(M, N, K, A, lda, B, ldb, C, ldc) -> int:

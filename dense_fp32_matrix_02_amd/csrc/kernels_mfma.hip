@@ -384,7 +384,8 @@ hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
 // letter A, second B); no ops suffix is the plain product.
 #define SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, KG, GM, LA, LB, TA, TB, SUFFIX)                       \
   {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, KIND_MFMA, BM, BN, BK,                \
-   64 * WM * WN * KG, TA, TB, &launch_mfma<MfmaCfg<BM, BN, BK, WM, WN, LA, LB, GM, KG>>}
+   64 * WM * WN * KG, TA, TB, &launch_mfma<MfmaCfg<BM, BN, BK, WM, WN, LA, LB, GM, KG>>,        \
+   reinterpret_cast<const void*>(&mfma_gemm_kernel<MfmaCfg<BM, BN, BK, WM, WN, LA, LB, GM, KG>>), KG}
 #define SGEMM_MFMA_N(BM, BN, BK, WM, WN) SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, 1, 4, KC, MC, 0, 0, "")
 #define SGEMM_MFMA_G8(BM, BN, BK, WM, WN) SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, 1, 8, KC, MC, 0, 0, "_g8")
 #define SGEMM_MFMA_K(BM, BN, BK, WM, WN) SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, 1, 4, KC, KM, 0, 0, "_bk")

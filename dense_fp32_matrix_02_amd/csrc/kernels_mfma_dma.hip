@@ -1,29 +1,31 @@
 // FP32 matrix-core GEMM kernels for gfx950 that stage the A and B slabs with
 // direct global-to-LDS loads (global_load_lds_dwordx4): each lane's 16 bytes
 // go from memory straight into LDS, with no register staging and no LDS store
-// instructions, which frees registers and issue slots in the K loop and lets
-// a third LDS stage fit next to a second workgroup on the compute unit.
+// instructions, which frees registers and issue slots in the K loop.
 //
 // Computation and block structure are those of the register-staged kernels
 // (a workgroup owns a BM x BN tile of C and marches K in BK-deep slabs; each
 // wave owns a register tile of 32x32 matrix-instruction accumulators; CUDA
-// Handbook section 17.3, GPU Parallel Book ch. 9 sections 9.4-9.7). Plain
-// product only: C = alpha * A.B + beta * C, A k-contiguous, B line-contiguous.
+// Handbook section 17.3, GPU Parallel Book ch. 9 sections 9.4-9.7), for
+// C = alpha * op(A).op(B) + beta * C with op(X) = X or X^T.
 //
-// LDS layouts (unpadded):
-//  * A slab [BM][BK]: row r holds k = 0..BK-1 in 16-byte chunks; chunk c is
-//    stored at position c ^ swz(r), which keeps the 128-bit fragment reads of
-//    eight consecutive rows in distinct banks;
-//  * B slab [BK][BN]: k-row by k-row, as in memory.
+// Each operand's slab has one of two LDS layouts, fixed by how the operand
+// lies in memory. Its "lines" are the rows of op(A) or the columns of op(B):
+//  * k-contiguous lines (A, and B^T): slab [ROWS][BK], 16-byte chunk c of
+//    line r stored at chunk position c ^ swz(r), which keeps the 128-bit
+//    fragment reads of eight consecutive lines in distinct banks;
+//  * line-contiguous k-rows (B, and A^T): slab [BK][ROWS], as in memory;
+//    fragments are four 32-bit reads of consecutive lines.
 // A direct load writes 64 lanes x 16 bytes to consecutive LDS addresses, so
 // the lane order is chosen to fill one 1 KiB region of the layout per
 // instruction; each lane fetches whichever global chunk belongs in its slot.
 //
 // Direct loads need 16-byte aligned global chunks that lie wholly inside the
-// matrices, and cannot zero k >= K. Problems whose N or K is not a multiple
-// of the tile, or whose operands are not 16-byte aligned, run a second
-// instantiation that stages every slab through registers instead (same
-// layouts, K tail zeroed in registers).
+// matrices, and cannot zero k >= K. Lines past the edge of C are clamped to
+// the last line (or the last whole chunk of lines), which feeds only outputs
+// that are never stored; K must be a whole number of slabs. Problems that do
+// not allow this run a second instantiation that stages every slab through
+// registers instead (same layouts, edges and K tail zeroed in registers).
 
 #include <type_traits>
 
@@ -54,50 +56,155 @@ __device__ __forceinline__ void copy16_to_lds(const float* g, float* lds) {
 // counters at their maximum (no wait).
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
-struct DmaCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
-  static constexpr int NW = WM * WN, NT = 64 * NW;
-  static constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
-  static constexpr int CPR = BK / 4;                 // 16-byte chunks per A row
-  static constexpr int A_FLOATS = BM * BK, B_FLOATS = BK * BN;
-  static constexpr int A_REGIONS = A_FLOATS / 256;   // 1 KiB regions per slab
-  static constexpr int B_REGIONS = B_FLOATS / 256;
-  static constexpr int A_PER_WAVE = A_REGIONS / NW, B_PER_WAVE = B_REGIONS / NW;
-  static constexpr int A_CHUNKS = A_FLOATS / 4 / NT, B_CHUNKS = B_FLOATS / 4 / NT;  // per thread
-  static constexpr int LDS_BYTES = 4 * STAGES * (A_FLOATS + B_FLOATS);
-  static_assert(BK == 16 || BK == 32, "A swizzle is defined for 16- and 32-deep slabs");
-  static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile must be 32x32 blocks");
-  static_assert(A_REGIONS % NW == 0 && B_REGIONS % NW == 0, "whole 1 KiB regions per wave");
-  static_assert((A_FLOATS / 4) % NT == 0 && (B_FLOATS / 4) % NT == 0, "whole chunks per thread");
-  static_assert(BN % 4 == 0 && STAGES >= 2, "slab shape");
-  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
-};
-
-// Position of chunk c of A row r: rows two (BK = 16) or one (BK = 32) 128-byte
-// bank spans apart get different chunk permutations.
+// Position of chunk c of a k-contiguous line r: lines two (BK = 16) or one
+// (BK = 32) 128-byte bank spans apart get different chunk permutations.
 template <int BK>
 __device__ __forceinline__ int swz(int r) {
   return BK == 16 ? (r >> 1) & 3 : r & 7;
 }
 
+// One operand's slab: ROWS lines by BK k values, staged by NW waves.
+// KCONTIG: the operand's lines are k-contiguous in memory (layout [ROWS][BK],
+// swizzled); otherwise its k-rows are line-contiguous (layout [BK][ROWS]).
+// X, ld: the stored matrix and its leading dimension; line0: first line of
+// the tile; extent: lines that exist (M for op(A), N for op(B)).
+template <int ROWS, int BK, bool KCONTIG, int NW>
+struct Slab {
+  static constexpr int NT = 64 * NW;
+  static constexpr int FLOATS = ROWS * BK;
+  static constexpr int REGIONS = FLOATS / 256;         // 1 KiB regions per slab
+  static constexpr int PER_WAVE = REGIONS / NW;        // direct loads per wave per slab
+  static constexpr int CHUNKS = FLOATS / 4 / NT;       // register-staged chunks per thread
+  static constexpr int CPL = KCONTIG ? BK / 4 : ROWS / 4;  // 16-byte chunks per LDS row
+  static_assert(!KCONTIG || BK == 16 || BK == 32, "swizzle is defined for 16- and 32-deep slabs");
+  static_assert(ROWS % 32 == 0 && REGIONS % NW == 0, "whole 1 KiB regions per wave");
+  static_assert((FLOATS / 4) % NT == 0, "whole chunks per thread");
+
+  // Global chunk that fills LDS slot `slot` (of 16 bytes) of the slab at k = 0.
+  // Direct loads only: the launcher guarantees 16-byte aligned chunks and, for
+  // line-contiguous operands, extent a multiple of 4.
+  __device__ static const float* direct_src(const float* X, int64_t ld, int line0, int extent, int slot) {
+    if constexpr (KCONTIG) {
+      const int r = slot / CPL;
+      const int chunk = (slot % CPL) ^ swz<BK>(r);
+      int line = line0 + r;
+      line = line < extent ? line : extent - 1;
+      return X + (int64_t)line * ld + 4 * chunk;
+    } else {
+      int col = line0 + 4 * (slot % CPL);
+      col = col <= extent - 4 ? col : extent - 4;
+      return X + (int64_t)(slot / CPL) * ld + col;
+    }
+  }
+  // Offset of the slab at k0 from the slab at k = 0.
+  __device__ static int64_t k_offset(int k0, int64_t ld) {
+    if constexpr (KCONTIG) return k0;
+    else return (int64_t)k0 * ld;
+  }
+
+  // Register staging: this thread's chunks of the slab at k0; with `tail`,
+  // k >= K reads as zero. Lines past the extent read as zero or repeat the
+  // last line (outputs that are never stored).
+  __device__ static void load(f32x4 (&r)[CHUNKS], const float* X, int64_t ld, int line0, int extent,
+                              int K, int k0, bool tail, int t) {
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+      const int idx = c * NT + t;
+      if constexpr (KCONTIG) {  // line idx / CPL, logical chunk idx % CPL
+        int line = line0 + idx / CPL;
+        line = line < extent ? line : extent - 1;
+        const int kc = k0 + 4 * (idx % CPL);
+        const float* s = X + (int64_t)line * ld + kc;
+        if (!tail || kc + 3 < K) {
+          r[c] = load16(s);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[c][e] = (kc + e < K) ? s[e] : 0.0f;
+        }
+      } else {  // k-row idx / CPL, chunk idx % CPL
+        const int kr = k0 + idx / CPL;
+        const int col = line0 + 4 * (idx % CPL);
+        const int valid = extent - col;
+        const float* s = X + (int64_t)kr * ld + (valid > 0 ? col : 0);
+        if (tail && kr >= K) {
+          r[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        } else if (valid >= 4) {
+          r[c] = load16(s);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[c][e] = (e < valid) ? s[e] : 0.0f;
+        }
+      }
+    }
+  }
+  __device__ static void store(float* lds, const f32x4 (&r)[CHUNKS], int t) {
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+      const int idx = c * NT + t;
+      if constexpr (KCONTIG) {
+        const int line = idx / CPL;
+        *reinterpret_cast<f32x4*>(lds + line * BK + 4 * ((idx % CPL) ^ swz<BK>(line))) = r[c];
+      } else {
+        *reinterpret_cast<f32x4*>(lds + (idx / CPL) * ROWS + 4 * (idx % CPL)) = r[c];
+      }
+    }
+  }
+
+  // Fragments. Lane (l32, h) of line block i reads line `line_w + 32 i + l32`
+  // at k = kk + 4h + u, u = 0..3. For k-contiguous lines that is logical chunk
+  // kk/4 + h, stored at (kk/4 + h) ^ swz(l32) (line_w and 32 i are multiples
+  // of 32); kk/4 is even, so the float offset is kk ^ key, key = 4 (h ^ swz).
+  __device__ static const float* frag_base(const float* lds, int line_w, int l32, int h) {
+    if constexpr (KCONTIG) return lds + (line_w + l32) * BK;
+    else return lds + 4 * h * ROWS + line_w + l32;
+  }
+  __device__ static int frag_key(int l32, int h) { return KCONTIG ? 4 * (h ^ swz<BK>(l32)) : 0; }
+  __device__ static f32x4 frag(const float* base, int i, int kk, int key) {
+    if constexpr (KCONTIG) {
+      return *reinterpret_cast<const f32x4*>(base + 32 * i * BK + (kk ^ key));
+    } else {
+      f32x4 v;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = base[(kk + u) * ROWS + 32 * i];
+      return v;
+    }
+  }
+};
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int TA_ = 0, int TB_ = 0>
+struct DmaCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  static constexpr int TA = TA_, TB = TB_;
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
+  // op(A) = A has k-contiguous rows; op(B) = B^T has k-contiguous columns.
+  using SlabA = Slab<BM, BK, TA == 0, NW>;
+  using SlabB = Slab<BN, BK, TB != 0, NW>;
+  static constexpr int LDS_BYTES = 4 * STAGES * (SlabA::FLOATS + SlabB::FLOATS);
+  static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile must be 32x32 blocks");
+  static_assert(STAGES >= 2 && STAGES <= 3, "two or three LDS stages");
+  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
+};
+
 // DIRECT: every slab by direct loads (the launcher guarantees 16-byte aligned
-// chunks, N a multiple of BN and K a multiple of BK); otherwise every slab
-// through registers. Two kernels rather than a branch, so each gets the registers it
-// needs.
+// chunks inside the matrices and K a multiple of BK); otherwise every slab
+// through registers. Two kernels rather than a branch, so each gets the
+// registers it needs.
 template <class Cfg, bool DIRECT>
 __global__ void __launch_bounds__(Cfg::NT) mfma_dma_kernel(GemmArgs g) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
-  constexpr int ST = Cfg::STAGES, CPR = Cfg::CPR;
+  constexpr int ST = Cfg::STAGES, NW = Cfg::NW;
+  using SA = typename Cfg::SlabA;
+  using SB = typename Cfg::SlabB;
   // One array per stage, selected at compile time: the compiler can then see
   // that a direct load into one stage does not alias reads of another, and
   // does not make those reads wait for the load.
-  __shared__ __attribute__((aligned(1024))) float As0[Cfg::A_FLOATS];
-  __shared__ __attribute__((aligned(1024))) float As1[Cfg::A_FLOATS];
-  __shared__ __attribute__((aligned(1024))) float As2[ST > 2 ? Cfg::A_FLOATS : 4];
-  __shared__ __attribute__((aligned(1024))) float Bs0[Cfg::B_FLOATS];
-  __shared__ __attribute__((aligned(1024))) float Bs1[Cfg::B_FLOATS];
-  __shared__ __attribute__((aligned(1024))) float Bs2[ST > 2 ? Cfg::B_FLOATS : 4];
+  __shared__ __attribute__((aligned(1024))) float As0[SA::FLOATS];
+  __shared__ __attribute__((aligned(1024))) float As1[SA::FLOATS];
+  __shared__ __attribute__((aligned(1024))) float As2[ST > 2 ? SA::FLOATS : 4];
+  __shared__ __attribute__((aligned(1024))) float Bs0[SB::FLOATS];
+  __shared__ __attribute__((aligned(1024))) float Bs1[SB::FLOATS];
+  __shared__ __attribute__((aligned(1024))) float Bs2[ST > 2 ? SB::FLOATS : 4];
   auto stage_a = [&](auto st) -> float* {
     if constexpr (decltype(st)::value == 0) return As0;
     else if constexpr (decltype(st)::value == 1) return As1;
@@ -125,97 +232,36 @@ __global__ void __launch_bounds__(Cfg::NT) mfma_dma_kernel(GemmArgs g) {
   const float* A = g.A + (int64_t)blockIdx.y * g.strideA;
   const float* B = g.B + (int64_t)blockIdx.y * g.strideB;
 
-
-  // ---- direct-load geometry: lane slot -> global chunk --------------------
-  // A region q (q = p*NW + wave) holds rows 256/BK*q ... of the slab; slot s
-  // of the region is row s / CPR, stored chunk s % CPR, loaded chunk
-  // (s % CPR) ^ swz(row). Rows beyond M are clamped (they feed no output).
-  const float* a_src[Cfg::A_PER_WAVE];
+  // ---- direct loads: region q = p*NW + wave of each slab is this wave's ----
+  const float* a_src[SA::PER_WAVE];
 #pragma unroll
-  for (int p = 0; p < Cfg::A_PER_WAVE; ++p) {
-    const int slot = (p * Cfg::NW + wave) * 64 + lane;
-    const int row = slot / CPR;
-    const int chunk = (slot % CPR) ^ swz<BK>(row);
-    int grow = m0 + row;
-    grow = grow < M ? grow : M - 1;
-    a_src[p] = A + (int64_t)grow * g.lda + 4 * chunk;
-  }
-  // B region q holds k-rows 256/BN*q ...; slot s is k-row s / (BN/4), chunk s % (BN/4).
-  const float* b_src[Cfg::B_PER_WAVE];
+  for (int p = 0; p < SA::PER_WAVE; ++p) a_src[p] = SA::direct_src(A, g.lda, m0, M, (p * NW + wave) * 64 + lane);
+  const float* b_src[SB::PER_WAVE];
 #pragma unroll
-  for (int p = 0; p < Cfg::B_PER_WAVE; ++p) {
-    const int slot = (p * Cfg::NW + wave) * 64 + lane;
-    b_src[p] = B + (int64_t)(slot / (BN / 4)) * g.ldb + n0 + 4 * (slot % (BN / 4));
-  }
+  for (int p = 0; p < SB::PER_WAVE; ++p) b_src[p] = SB::direct_src(B, g.ldb, n0, N, (p * NW + wave) * 64 + lane);
   auto issue_direct = [&](int k0, auto stage) {
     float* as = stage_a(stage);
     float* bs = stage_b(stage);
+    const int64_t oa = SA::k_offset(k0, g.lda), ob = SB::k_offset(k0, g.ldb);
 #pragma unroll
-    for (int p = 0; p < Cfg::A_PER_WAVE; ++p)
-      copy16_to_lds(a_src[p] + k0, as + (p * Cfg::NW + wave) * 256);
+    for (int p = 0; p < SA::PER_WAVE; ++p) copy16_to_lds(a_src[p] + oa, as + (p * NW + wave) * 256);
 #pragma unroll
-    for (int p = 0; p < Cfg::B_PER_WAVE; ++p)
-      copy16_to_lds(b_src[p] + (int64_t)k0 * g.ldb, bs + (p * Cfg::NW + wave) * 256);
+    for (int p = 0; p < SB::PER_WAVE; ++p) copy16_to_lds(b_src[p] + ob, bs + (p * NW + wave) * 256);
   };
 
   // ---- register staging (edge tiles, unaligned operands, the K tail) ------
-  f32x4 ra[Cfg::A_CHUNKS], rb[Cfg::B_CHUNKS];
+  f32x4 ra[SA::CHUNKS], rb[SB::CHUNKS];
   auto load_regs = [&](int k0, bool tail) {
-#pragma unroll
-    for (int c = 0; c < Cfg::A_CHUNKS; ++c) {
-      const int idx = c * Cfg::NT + t;  // row idx / CPR, logical chunk idx % CPR
-      int grow = m0 + idx / CPR;
-      grow = grow < M ? grow : M - 1;
-      const int kc = k0 + 4 * (idx % CPR);
-      const float* s = A + (int64_t)grow * g.lda + kc;
-      if (!tail || kc + 3 < K) {
-        ra[c] = load16(s);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ra[c][e] = (kc + e < K) ? s[e] : 0.0f;
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < Cfg::B_CHUNKS; ++c) {
-      const int idx = c * Cfg::NT + t;  // k-row idx / (BN/4), chunk idx % (BN/4)
-      const int kr = k0 + idx / (BN / 4);
-      const int col = n0 + 4 * (idx % (BN / 4));
-      const int valid = N - col;
-      const float* s = B + (int64_t)kr * g.ldb + (valid > 0 ? col : 0);
-      if (tail && kr >= K) {
-        rb[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      } else if (valid >= 4) {
-        rb[c] = load16(s);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rb[c][e] = (e < valid) ? s[e] : 0.0f;
-      }
-    }
+    SA::load(ra, A, g.lda, m0, M, K, k0, tail, t);
+    SB::load(rb, B, g.ldb, n0, N, K, k0, tail, t);
   };
   auto store_regs = [&](auto stage) {
-    float* as = stage_a(stage);
-    float* bs = stage_b(stage);
-#pragma unroll
-    for (int c = 0; c < Cfg::A_CHUNKS; ++c) {
-      const int idx = c * Cfg::NT + t;
-      const int row = idx / CPR;
-      *reinterpret_cast<f32x4*>(as + row * BK + 4 * ((idx % CPR) ^ swz<BK>(row))) = ra[c];
-    }
-#pragma unroll
-    for (int c = 0; c < Cfg::B_CHUNKS; ++c) {
-      const int idx = c * Cfg::NT + t;
-      *reinterpret_cast<f32x4*>(bs + (idx / (BN / 4)) * BN + 4 * (idx % (BN / 4))) = rb[c];
-    }
+    SA::store(stage_a(stage), ra, t);
+    SB::store(stage_b(stage), rb, t);
   };
 
   // ---- fragments and the inner product ------------------------------------
-  // Lane (l32, h) of block row i reads A row r = wm*WTM + 32i + l32 at logical
-  // chunk kk/4 + h, stored at chunk (kk/4 + h) ^ swz(r); swz(r) = swz(l32)
-  // because 32i and wm*WTM are multiples of 32. kk/4 is even, so
-  // (kk/4 + h) ^ swz = (kk/4) ^ (h ^ swz) and the float offset is kk ^ akey.
-  const int a_row = wm * Cfg::WTM + l32;
-  const int akey = 4 * (h ^ swz<BK>(l32));
-  const int b_col = wn * Cfg::WTN + l32;
+  const int akey = SA::frag_key(l32, h), bkey = SB::frag_key(l32, h);
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -225,17 +271,15 @@ __global__ void __launch_bounds__(Cfg::NT) mfma_dma_kernel(GemmArgs g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   auto compute = [&](auto stage) {
-    const float* as = stage_a(stage) + a_row * BK;
-    const float* bs = stage_b(stage) + (4 * h) * BN + b_col;
+    const float* as = SA::frag_base(stage_a(stage), wm * Cfg::WTM, l32, h);
+    const float* bs = SB::frag_base(stage_b(stage), wn * Cfg::WTN, l32, h);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 8) {
       f32x4 af[FM], bf[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const f32x4*>(as + 32 * i * BK + (kk ^ akey));
+      for (int i = 0; i < FM; ++i) af[i] = SA::frag(as, i, kk, akey);
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) bf[j][u] = bs[(kk + u) * BN + 32 * j];
+      for (int j = 0; j < FN; ++j) bf[j] = SB::frag(bs, j, kk, bkey);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -268,7 +312,7 @@ __global__ void __launch_bounds__(Cfg::NT) mfma_dma_kernel(GemmArgs g) {
       compute(cur);
       if constexpr (ST == 3) {
         // Slab s+1 must have landed; slab s+2's loads may stay in flight.
-        constexpr int per_slab = Cfg::A_PER_WAVE + Cfg::B_PER_WAVE;
+        constexpr int per_slab = SA::PER_WAVE + SB::PER_WAVE;
         static_assert(per_slab <= 15, "vmcnt field");
         if (more) __builtin_amdgcn_s_waitcnt(0x0F70 | per_slab);
         else wait_loads();
@@ -337,33 +381,47 @@ __global__ void __launch_bounds__(Cfg::NT) mfma_dma_kernel(GemmArgs g) {
 
 // Direct loads need every 16-byte chunk they fetch to be aligned and inside
 // the matrices: A and B (and each batch entry) 16-byte aligned, leading
-// dimensions multiples of 4, and no tile crossing the right edge of C. The
+// dimensions multiples of 4, and the extent of a line-contiguous operand (M
+// for A^T, N for B) a multiple of 4 so the last chunk of lines is whole. The
 // direct kernel also takes K (and a short last split-K chunk) in whole slabs,
 // which keeps the K tail, and its registers, out of it.
 template <class Cfg>
+bool direct_ok(const GemmArgs& g) {
+  const bool aligned = ((reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B)) & 15) == 0 &&
+                       ((g.lda | g.ldb) & 3) == 0 && (g.batch <= 1 || ((g.strideA | g.strideB) & 3) == 0);
+  const bool lines = (Cfg::TA == 0 || g.M % 4 == 0) && (Cfg::TB != 0 || g.N % 4 == 0);
+  return g.M > 0 && g.N > 0 && aligned && lines && g.K % Cfg::BK == 0 && g.k_last % Cfg::BK == 0;
+}
+
+template <class Cfg>
 hipError_t launch_mfma_dma(const GemmArgs& g, hipStream_t stream) {
   const int64_t tiles = (int64_t)((g.M + Cfg::BM - 1) / Cfg::BM) * ((g.N + Cfg::BN - 1) / Cfg::BN);
-  const bool direct = ((reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B)) & 15) == 0 &&
-                      ((g.lda | g.ldb) & 3) == 0 && (g.batch <= 1 || ((g.strideA | g.strideB) & 3) == 0) &&
-                      g.N % Cfg::BN == 0 && g.K % Cfg::BK == 0 && g.k_last % Cfg::BK == 0;
   GemmArgs a = g;
   void* args[] = {&a};
-  const void* kernel = direct ? reinterpret_cast<const void*>(&mfma_dma_kernel<Cfg, true>)
-                              : reinterpret_cast<const void*>(&mfma_dma_kernel<Cfg, false>);
+  const void* kernel = direct_ok<Cfg>(g) ? reinterpret_cast<const void*>(&mfma_dma_kernel<Cfg, true>)
+                                         : reinterpret_cast<const void*>(&mfma_dma_kernel<Cfg, false>);
   return hipLaunchKernel(kernel, dim3((unsigned)tiles, (unsigned)g.batch), dim3(Cfg::NT), args, 0, stream);
 }
 
 }  // namespace
 
-// Name: mfma32_<BM>x<BN>x<BK>_w<WM>x<WN>_lds<STAGES>: direct global-to-LDS
-// staging with STAGES LDS buffers; plain product only.
-#define SGEMM_MFMA_DMA(BM, BN, BK, WM, WN, ST)                                                       \
-  {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_lds" #ST, KIND_MFMA, BM, BN, BK, 64 * WM * WN, 0, \
-   0, &launch_mfma_dma<DmaCfg<BM, BN, BK, WM, WN, ST>>}
+// Name: mfma32_<BM>x<BN>x<BK>_w<WM>x<WN>_lds<STAGES>[_<ops>]: direct
+// global-to-LDS staging with STAGES LDS buffers; <ops> = tn, nt or tt names
+// transposed operands (first letter A, second B), none the plain product.
+#define SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, ST, TA, TB, SFX)                                        \
+  {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_lds" #ST SFX, KIND_MFMA, BM, BN, BK, 64 * WM * WN, \
+   TA, TB, &launch_mfma_dma<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB>>,                                  \
+   reinterpret_cast<const void*>(&mfma_dma_kernel<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB>, true>), 1}
+#define SGEMM_MFMA_DMA(BM, BN, BK, WM, WN, ST) SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, ST, 0, 0, "")
+#define SGEMM_MFMA_DMA_OPS(BM, BN, BK, WM, WN, ST)                      \
+  SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, ST, 1, 0, "_tn"),              \
+      SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, ST, 0, 1, "_nt"),          \
+      SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, ST, 1, 1, "_tt")
 
 KernelConfig kMfmaDmaConfigs[] = {
     // 256x256 block tile, 16 waves of 64x64, two stages: one workgroup per CU
     SGEMM_MFMA_DMA(256, 256, 16, 4, 4, 2),
+    SGEMM_MFMA_DMA_OPS(256, 256, 16, 4, 4, 2),
 };
 const int kNumMfmaDmaConfigs = sizeof(kMfmaDmaConfigs) / sizeof(kMfmaDmaConfigs[0]);
 

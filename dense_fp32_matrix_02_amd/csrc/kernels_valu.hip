@@ -240,7 +240,8 @@ hipError_t launch_valu(const GemmArgs& g, hipStream_t stream) {
 // tile BM x BN, registers bounded for at least W waves per SIMD (default 1).
 #define SGEMM_VALU_CFG(BM, BN, BK, TM, W, SUFFIX)                                                        \
   {"valu" #TM "x8_" #BM "x" #BN "x" #BK SUFFIX, KIND_VALU, BM, BN, BK, (BM / TM) * (BN / 8), 0, 0, \
-   &launch_valu<ValuCfg<BM, BN, BK, TM, 4, W>>}
+   &launch_valu<ValuCfg<BM, BN, BK, TM, 4, W>>,                                                        \
+   reinterpret_cast<const void*>(&valu_gemm_kernel<ValuCfg<BM, BN, BK, TM, 4, W>>), 1}
 
 KernelConfig kValuConfigs[] = {
     SGEMM_VALU_CFG(128, 128, 8, 8, 1, ""),

@@ -10,18 +10,32 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "sgemm_internal.h"
 
 namespace sgemm_impl {
 namespace {
 
-struct ShapeEntry {
+// The measured tile table (tile_table.inc, written by tune.py): per op pair,
+// the candidate configurations with their occupancy, the measured shapes,
+// and each candidate's median time at each shape (0: not a candidate there).
+struct TableConfig {
+  const char* name;
+  int occupancy;  // workgroups one compute unit holds at once
+};
+struct TableShape {
   int M, N, K;
-  const char* config;
+};
+struct TableBlock {
+  int opA, opB;
+  int ncand, nshapes;
+  const TableConfig* cand;
+  const TableShape* shapes;
+  const float* times_us;  // nshapes x ncand, row-major
 };
 #include "tile_table.inc"
-constexpr int kTableEntries = sizeof(kShapeTable) / sizeof(kShapeTable[0]) - 1;  // without the sentinel
+constexpr int kNumTableBlocks = sizeof(kTableBlocks) / sizeof(kTableBlocks[0]);
 
 constexpr int kCompute = 256;  // compute units on MI355X
 
@@ -95,23 +109,56 @@ const char* ops_suffix(int opA, int opB) {
 // Configuration names used by the selection, resolved to ids once per
 // process (a function-local static: initialised on first use, thread-safe,
 // never written afterwards), so a call costs no string comparisons.
-// Direct-to-LDS kernel the selection switches to for plain products that
-// qualify for direct loads (16-byte aligned operands, N a multiple of its
-// 256-wide tile, K a multiple of its 16-deep slab) and whose grid fills the
-// chip: at least one 256x256 tile per compute unit, at least kRuleMinFill of
-// the padded tile grid useful, and at least kDirectMinWave of the last wave
-// of workgroups occupied. Measured on the tuning grid it is never slower than
-// the best register-staged configuration there (2.3% faster on average, up to
-// 145.7 against 141.2 TFLOP/s); below one tile per CU it loses up to 45%.
-const char* const kDirectConfig = "mfma32_256x256x16_w4x4_lds2";
+// Direct-to-LDS kernels the rule switches to (per op pair; the transposed-B
+// form has none: its register-staged 256x256x32 tile is as fast) for
+// problems that qualify for direct loads and whose grid fills the chip: at
+// least one 256x256 tile per compute unit, at least kRuleMinFill of the
+// padded tile grid useful, and at least kDirectMinWave of the last wave of
+// workgroups occupied. Measured at 4096^3 to 8192^3 and on non-square shapes
+// of that size, they are 2-5% faster than the register-staged tiles there.
+const char* const kDirectConfig[2][2] = {{"mfma32_256x256x16_w4x4_lds2", nullptr},
+                                         {"mfma32_256x256x16_w4x4_lds2_tn", "mfma32_256x256x16_w4x4_lds2_tt"}};
 constexpr double kDirectMinWave = 0.9;
+
+// The table resolved for the model selection below: each candidate's
+// configuration id and occupancy, and each measured
+// time divided by the model's busy time at its own shape (0: no candidate).
+struct ResolvedBlock {
+  const TableBlock* src = nullptr;
+  int ids[64];
+  int occ[64];
+  std::vector<double> norm;  // nshapes x ncand
+};
 
 struct Resolved {
   int rule[2][2][kRuleTileCount];  // -1 where a configuration is not built
   int small[2][2][2];              // [opA][opB][long K]
-  int direct;                      // kDirectConfig
-  int table[kTableEntries];         // id of each table entry (-1 if unknown)
+  int direct[2][2];                // kDirectConfig (-1: none)
+  ResolvedBlock block[2][2];
 };
+
+bool is_direct_config(int id) { return id >= kNumMfmaConfigs && id < kNumMfmaConfigs + kNumMfmaDmaConfigs; }
+
+// Fill model of a launch of configuration c on an M x N x K problem (batch
+// entries in grid.y): workgroups are dealt round-robin over the XCDs and
+// their compute units, so the busiest CU gets n = ceil(workgroups / 256) of
+// them. It runs them `occ` at a time, at full rate only while at least
+// kSatChains independent 32x32 accumulator blocks are resident (two per
+// SIMD, so one block's matrix instructions, or its wave's loads, overlap
+// another's); with b < kSatChains resident, a workgroup takes kSatChains / b
+// times as long. A workgroup holds kgroups * (BM/32) * (BN/32) blocks. The
+// busy time, in units of one workgroup slab step at full rate, is
+//   n * max(1, kSatChains / (min(n, occ) * blocks per workgroup)) * ceil(K / BK).
+constexpr int kSatChains = 8;
+
+double busy_time(const KernelConfig& c, int occ, int M, int N, int K, int batch) {
+  const int64_t wgs = tiles_for(c, M, N) * (int64_t)(batch < kMaxGridY ? batch : kMaxGridY);
+  const int64_t n = (wgs + kCompute - 1) / kCompute;
+  const int64_t blocks = (int64_t)(c.kgroups > 0 ? c.kgroups : 1) * (c.bm / 32) * (c.bn / 32);
+  const int64_t resident = (n < occ ? n : occ) * blocks;
+  const double stretch = resident >= kSatChains ? 1.0 : (double)kSatChains / (double)resident;
+  return (double)n * stretch * (double)(((int64_t)K + c.bk - 1) / c.bk);
+}
 
 const Resolved& resolved() {
   static const Resolved r = [] {
@@ -124,9 +171,31 @@ const Resolved& resolved() {
           std::snprintf(name, sizeof(name), "mfma32_%s%s", l ? kRuleSmallLongK : kRuleSmall, ops_suffix(a, b));
           x.small[a][b][l] = config_id(name);
         }
+        x.direct[a][b] = kDirectConfig[a][b] ? config_id(kDirectConfig[a][b]) : -1;
       }
-    for (int t = 0; t < kTableEntries; ++t) x.table[t] = config_id(kShapeTable[t].config);
-    x.direct = config_id(kDirectConfig);
+    for (int t = 0; t < kNumTableBlocks; ++t) {
+      const TableBlock& tb = kTableBlocks[t];
+      if (tb.opA < 0 || tb.opA > 1 || tb.opB < 0 || tb.opB > 1 || tb.ncand > 64) continue;
+      ResolvedBlock& rb = x.block[tb.opA][tb.opB];
+      rb.src = &tb;
+      for (int c = 0; c < tb.ncand; ++c) {
+        int id = config_id(tb.cand[c].name);
+        const KernelConfig* cfg = config_at(id);
+        if (cfg && (cfg->transA != tb.opA || cfg->transB != tb.opB || cfg->kind != KIND_MFMA)) id = -1;
+        rb.ids[c] = id;
+        rb.occ[c] = tb.cand[c].occupancy > 0 ? tb.cand[c].occupancy : 1;
+      }
+      rb.norm.assign((size_t)tb.nshapes * tb.ncand, 0.0);
+      for (int s = 0; s < tb.nshapes; ++s) {
+        const TableShape& e = tb.shapes[s];
+        for (int c = 0; c < tb.ncand; ++c) {
+          const float t_us = tb.times_us[(size_t)s * tb.ncand + c];
+          const KernelConfig* cfg = config_at(rb.ids[c]);
+          if (cfg && t_us > 0.0f)
+            rb.norm[(size_t)s * tb.ncand + c] = t_us / busy_time(*cfg, rb.occ[c], e.M, e.N, e.K, 1);
+        }
+      }
+    }
     return x;
   }();
   return r;
@@ -148,45 +217,69 @@ int rule_select(int opA, int opB, int M, int N, int K, int batch) {
   return rs.small[opA][opB][K >= kRuleLongK ? 1 : 0];
 }
 
-// Table lookup for the plain product: the measured entry of the same shape,
-// else the measured entry nearest in (log M, log N, log K) provided it lies
-// within a factor of two in each dimension; -1 when none qualifies.
-int table_select(int M, int N, int K) {
+// Whether direct-to-LDS configuration c takes its direct path on this
+// problem (its launcher's condition, with `aligned` standing for the pointer,
+// leading-dimension and stride alignment): otherwise it stages through
+// registers, which its measured times do not describe.
+bool direct_path(const KernelConfig& c, int M, int N, int K, bool aligned) {
+  return aligned && M > 0 && N > 0 && K > 0 && K % c.bk == 0 && (!c.transA || M % 4 == 0) &&
+         (c.transB || N % 4 == 0);
+}
+
+// Model selection for a single product: the measured shape of this op pair
+// nearest (M, N, K) in (log M, log N, log K), among those within a factor of
+// two in every dimension (the first on a tie); then the candidate with the
+// least predicted time, each candidate's measured time there scaled by the
+// ratio of busy_time at (M, N, K) to busy_time at the measured shape (the
+// first on a tie). -1 when no measured shape qualifies.
+int model_select(int opA, int opB, int M, int N, int K, bool aligned) {
   if (M <= 0 || N <= 0 || K <= 0) return -1;
-  const int* ids = resolved().table;
-  int best = -1;
-  double best_d = 1e30;
-  for (int t = 0; t < kTableEntries; ++t) {
-    const ShapeEntry* e = &kShapeTable[t];
-    const int id = ids[t];
-    if (id < 0) continue;
-    if (e->M == M && e->N == N && e->K == K) return id;
+  const ResolvedBlock& rb = resolved().block[opA][opB];
+  if (!rb.src) return -1;
+  const TableBlock& tb = *rb.src;
+  int near = -1;
+  double near_d = 1e30;
+  for (int s = 0; s < tb.nshapes; ++s) {
+    const TableShape& e = tb.shapes[s];
     // within a factor of two in every dimension (integer test before any log)
-    if ((int64_t)M > 2LL * e->M || (int64_t)e->M > 2LL * M || (int64_t)N > 2LL * e->N ||
-        (int64_t)e->N > 2LL * N || (int64_t)K > 2LL * e->K || (int64_t)e->K > 2LL * K)
+    if ((int64_t)M > 2LL * e.M || (int64_t)e.M > 2LL * M || (int64_t)N > 2LL * e.N ||
+        (int64_t)e.N > 2LL * N || (int64_t)K > 2LL * e.K || (int64_t)e.K > 2LL * K)
       continue;
-    const double dm = std::fabs(std::log2((double)M / e->M));
-    const double dn = std::fabs(std::log2((double)N / e->N));
-    const double dk = std::fabs(std::log2((double)K / e->K));
-    if (dm > 1.0 || dn > 1.0 || dk > 1.0) continue;
-    const double d = dm + dn + dk;
-    if (d < best_d) {
-      best_d = d;
+    const double d = std::fabs(std::log2((double)M / e.M)) + std::fabs(std::log2((double)N / e.N)) +
+                     std::fabs(std::log2((double)K / e.K));
+    if (d < near_d) {
+      near_d = d;
+      near = s;
+    }
+  }
+  if (near < 0) return -1;
+  int best = -1;
+  double best_t = 0.0;
+  for (int c = 0; c < tb.ncand; ++c) {
+    const double norm = rb.norm[(size_t)near * tb.ncand + c];
+    if (norm <= 0.0) continue;
+    const int id = rb.ids[c];
+    const KernelConfig& cfg = *config_at(id);
+    if (is_direct_config(id) && !direct_path(cfg, M, N, K, aligned)) continue;
+    const double t = norm * busy_time(cfg, rb.occ[c], M, N, K, 1);
+    if (best < 0 || t < best_t) {
       best = id;
+      best_t = t;
     }
   }
   return best;
 }
 
-// kDirectConfig in place of `id` when the problem qualifies (see above).
-// `aligned`: the operands allow 16-byte direct loads (callers that do not
-// know the pointers pass true; the kernel's launcher checks again and stages
-// through registers when they do not).
+// The op pair's direct-to-LDS configuration in place of `id` when the
+// problem qualifies (see kDirectConfig). `aligned`: the operands allow
+// 16-byte direct loads (callers that do not know the pointers pass true; the
+// kernel's launcher checks again and stages through registers when they do
+// not).
 int upgrade_direct(int id, int opA, int opB, int M, int N, int K, int batch, bool aligned) {
-  const int did = resolved().direct;
-  if (did < 0 || opA || opB || !aligned || M <= 0 || K <= 0) return id;
+  const int did = resolved().direct[opA][opB];
+  if (did < 0) return id;
   const KernelConfig& c = *config_at(did);
-  if (N % c.bn != 0 || K % c.bk != 0) return id;
+  if (!direct_path(c, M, N, K, aligned)) return id;
   const int64_t tiles = tiles_for(c, M, N);
   const int64_t wgs = tiles * (batch < kMaxGridY ? batch : kMaxGridY);
   const double fill = (double)M * N / ((double)tiles * c.bm * c.bn);
@@ -194,11 +287,14 @@ int upgrade_direct(int id, int opA, int opB, int M, int N, int K, int batch, boo
   return (wgs >= kCompute && fill >= kRuleMinFill && wave >= kDirectMinWave) ? did : id;
 }
 
+// Single products go to the model selection; batches, and shapes with no
+// measured shape nearby, to the rule (then the direct-kernel switch).
 int select_mfma(int opA, int opB, int M, int N, int K, int batch, bool aligned = true) {
-  int id = -1;
-  if (!opA && !opB && batch == 1) id = table_select(M, N, K);
-  if (id < 0) id = rule_select(opA, opB, M, N, K, batch);
-  return upgrade_direct(id, opA, opB, M, N, K, batch, aligned);
+  if (batch == 1) {
+    const int id = model_select(opA, opB, M, N, K, aligned);
+    if (id >= 0) return id;
+  }
+  return upgrade_direct(rule_select(opA, opB, M, N, K, batch), opA, opB, M, N, K, batch, aligned);
 }
 
 // Vector-kernel configurations the selection considers, largest block tile
@@ -544,6 +640,19 @@ int sgemm_mi355_config_info(int config, int* bm, int* bn, int* bk, int* threads)
   return SGEMM_MI355_OK;
 }
 
+int sgemm_mi355_config_occupancy(int config, int* workgroups_per_cu) {
+  const KernelConfig* c = config_at(config);
+  if (!c) return SGEMM_MI355_ERR_CONFIG;
+  if (!workgroups_per_cu) return SGEMM_MI355_ERR_NULL;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, c->kernel, c->threads, 0) != hipSuccess) {
+    (void)hipGetLastError();  // leave no sticky error for the caller's next HIP call
+    return SGEMM_MI355_ERR_LAUNCH;
+  }
+  *workgroups_per_cu = n;
+  return SGEMM_MI355_OK;
+}
+
 int sgemm_mi355_config_ops(int config, int* opA, int* opB) {
   const KernelConfig* c = config_at(config);
   if (!c) return SGEMM_MI355_ERR_CONFIG;
@@ -578,6 +687,6 @@ const char* sgemm_mi355_strerror(int code) {
   }
 }
 
-const char* sgemm_mi355_version(void) { return "0.4.0"; }
+const char* sgemm_mi355_version(void) { return "0.5.0"; }
 
 }  // extern "C"

@@ -38,6 +38,8 @@ struct KernelConfig {
   int threads;
   int transA, transB;  // operand layouts the kernel reads
   LaunchFn launch;
+  const void* kernel;  // the kernel launch() runs for 16-byte aligned operands (occupancy queries)
+  int kgroups;         // wave groups that split each slab's k range (1: none)
 };
 
 // Host-only tables (not const: a const global would also be emitted for the

@@ -3,19 +3,23 @@ shape and emit the tile table the library compiles in.
 
 The best tile is found by measurement, not derived (CUDA Handbook section
 17.3 sweeps the microtile; GPU Parallel Book ch. 9, section 9.6 sweeps the
-occupancy setting). For each shape every matrix-core configuration runs on
-seeded U[-1,1) inputs; the median of `reps` event-timed launches decides.
+occupancy setting). For each shape every matrix-core configuration built for
+the op pair runs on seeded U[-1,1) inputs; the median of `reps` event-timed
+launches is recorded, with each configuration's occupancy (workgroups per
+compute unit, from the HIP runtime).
 
     python -m dense_fp32_matrix_02_amd.tune [--shapes 8192x8192x8192,...]
-        [--reps 20] [--json results.json] [--table tile_table.inc]
+        [--grid] [--reps 20] [--json results.json] [--table tile_table.inc]
         [--ops nn|tn|nt|tt] [--batch B]
+    python -m dense_fp32_matrix_02_amd.tune --from-json nn.json,tn.json,nt.json,tt.json \
+        --table dense_fp32_matrix_02_amd/csrc/tile_table.inc
 
-``--table`` writes a tile_table.inc with one exact-shape entry per measured
-shape; copy it to csrc/ and rebuild to use it. ``--ops`` times the
-configurations built for transposed operands (op(A) = A^T for a first letter
-t, op(B) = B^T for a second), on operands stored transposed; ``--batch``
-times strided batches of B independent products per launch. The table holds
-plain single products only, so ``--table`` needs the defaults of both.
+``--ops`` times the configurations built for transposed operands (op(A) =
+A^T for a first letter t, op(B) = B^T for a second), on operands stored
+transposed; ``--batch`` times strided batches of B independent products per
+launch. ``--table`` writes the table from the single products measured (this
+run's, or the saved ``--from-json`` results of one file per op pair); copy it
+to csrc/ and rebuild to use it.
 """
 from __future__ import annotations
 
@@ -31,20 +35,31 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 TABLE_HEADER = """\
-// Tile-configuration table: which kernel configuration each problem shape
-// uses. The best tile is an empirical question (CUDA Handbook section 17.3:
-// the microtile is chosen by sweeping; GPU Parallel Book section 9.6: the
-// occupancy setting is found by measurement), so each entry records the
-// fastest register-staged configuration measured on MI355X for one shape
-// (the direct-to-LDS kernel is chosen by rule on top, for problems that
-// qualify). A shape without its own entry takes the nearest measured shape
-// (in log M, log N, log K, within a factor of two in each), else the rule in
-// sgemm_api.hip.
+// Tile-configuration table: measured run times of the kernel configurations
+// on a grid of problem shapes, per op pair. The best tile is an empirical
+// question (CUDA Handbook section 17.3: the microtile is chosen by sweeping;
+// GPU Parallel Book section 9.6: the occupancy setting is found by
+// measurement). The selection takes the measured shape nearest a problem (in
+// log M, log N, log K, within a factor of two in each) and scales each
+// configuration's time there to the problem with a model of how its
+// workgroups fill the compute units (sgemm_api.hip); the fastest predicted
+// configuration runs.
+//
+// Per op pair: the candidates (configurations that are the fastest on at
+// least one measured shape) with their occupancy (workgroups one compute
+// unit holds, from the HIP runtime), then per shape {{M, N, K}} and the
+// candidates' median times in microseconds; 0 marks a time more than
+// {cut}x the shape's best (never a candidate there).
 //
 // Written by dense_fp32_matrix_02_amd/tune.py (median of {reps} launches per
-// configuration). Format: {{M, N, K, "configuration name"}}.
-static const ShapeEntry kShapeTable[] = {{
+// configuration and shape).
 """
+
+# Times more than this factor above a shape's best are stored as 0 (not a
+# candidate at that shape): the fill model never scales one configuration
+# against another by as much at a neighbouring shape.
+TABLE_CUT = 2.0
+OPS_NAMES = ("nn", "nt", "tn", "tt")
 
 
 def parse_shapes(text):
@@ -125,14 +140,17 @@ def main(argv=None):
     ap.add_argument("--batch", type=int, default=1)
     args = ap.parse_args(argv)
     opA, opB = int(args.ops[0] == "t"), int(args.ops[1] == "t")
-    if args.table and (opA or opB or args.batch != 1):
-        ap.error("--table records plain single products: leave --ops and --batch at their defaults")
+    if args.table and args.batch != 1:
+        ap.error("--table records single products: leave --batch at 1")
     if args.splitk and (opA or opB or args.batch != 1):
         ap.error("--splitk times plain single products")
 
     if args.from_json:
-        with open(args.from_json) as f:
-            write_table(json.load(f), args.table, args.reps)
+        results = []
+        for path in args.from_json.split(","):
+            with open(path) as f:
+                results += json.load(f)
+        write_table(results, args.table, args.reps)
         return
 
     names = sg.config_names()
@@ -147,10 +165,12 @@ def main(argv=None):
         sides = [128, 256, 512, 1024, 2048, 4096, 8192]
         shapes += [(m, n, k) for m in sides for n in sides for k in (256, 1024, 4096, 16384)
                    if (m, n, k) not in shapes]
+    occupancy = {names[cid]: sg.sgemm_mi355_config_occupancy(cid) for cid in cands}
     tag = ("" if args.ops == "nn" else f" {args.ops}") + ("" if args.batch == 1 else f" x{args.batch}")
     for (M, N, K) in shapes:
         Ad, Bd, C = make_inputs(M, N, K, opA, opB, args.batch)
-        row = {"M": M, "N": N, "K": K, "ops": args.ops, "batch": args.batch, "times_ms": {}}
+        row = {"M": M, "N": N, "K": K, "ops": args.ops, "batch": args.batch, "times_ms": {},
+               "occupancy": occupancy}
         flops = 2 * M * N * K * args.batch
         for cid in cands:
             ms = time_call(config_call(Ad, Bd, C, cid, opA, opB, args.batch), args.reps, args.warmup)
@@ -180,17 +200,50 @@ def main(argv=None):
 
 
 def write_table(results, path, reps):
-    """One entry per measured shape: the fastest register-staged configuration.
-    Direct-to-LDS configurations (_lds) are left out: the library switches to
-    them by rule, only for problems that qualify for direct loads, so a
-    nearest-shape lookup never lands on one for a problem that does not."""
+    """The tile table from single-product rows of any op pairs: per op pair,
+    the configurations that are fastest on at least one shape, their
+    occupancy, and each shape's times (0 beyond TABLE_CUT x its best)."""
     with open(path, "w") as f:
-        f.write(TABLE_HEADER.format(reps=reps))
-        for r in results:
-            t = {n: ms for n, ms in r["times_ms"].items() if n.startswith("mfma") and "_lds" not in n}
-            if t:
-                f.write(f'    {{{r["M"]}, {r["N"]}, {r["K"]}, "{min(t, key=t.get)}"}},\n')
-        f.write("    {0, 0, 0, nullptr},  // sentinel\n};\n")
+        f.write(TABLE_HEADER.format(reps=reps, cut=TABLE_CUT))
+        blocks = []
+        for ops in OPS_NAMES:
+            rows = [r for r in results if r.get("ops", "nn") == ops and r.get("batch", 1) == 1]
+            rows = [r for r in rows if any(n.startswith("mfma") for n in r["times_ms"])]
+            if not rows:
+                continue
+            occ = {}
+            for r in rows:
+                occ.update(r.get("occupancy", {}))
+            best = [min((n for n in r["times_ms"] if n.startswith("mfma")), key=r["times_ms"].get) for r in rows]
+            cands = sorted(set(best), key=best.index)
+            missing = [n for n in cands if n not in occ]
+            if missing:
+                raise ValueError(f"no occupancy recorded for {missing} ({ops})")
+            f.write(f"\n// op pair {ops}: {len(cands)} candidates, {len(rows)} shapes\n")
+            f.write(f"static const TableConfig kCand_{ops}[] = {{\n")
+            for n in cands:
+                f.write(f'    {{"{n}", {occ[n]}}},\n')
+            f.write("};\n")
+            f.write(f"static const TableShape kShapes_{ops}[] = {{\n")
+            for r in rows:
+                f.write(f'    {{{r["M"]}, {r["N"]}, {r["K"]}}},\n')
+            f.write("};\n")
+            f.write(f"static const float kTimes_{ops}[] = {{\n")
+            for r in rows:
+                t = r["times_ms"]
+                b = min(t[n] for n in t if n.startswith("mfma"))
+                cells = []
+                for n in cands:
+                    v = t.get(n)
+                    cells.append("0" if v is None or v > TABLE_CUT * b else f"{v * 1e3:.5g}")
+                f.write("    " + ", ".join(cells) + ",\n")
+            f.write("};\n")
+            blocks.append((ops, len(cands), len(rows)))
+        f.write("\nstatic const TableBlock kTableBlocks[] = {\n")
+        for ops, nc, nr in blocks:
+            f.write(f"    {{{int(ops[0] == 't')}, {int(ops[1] == 't')}, {nc}, {nr}, kCand_{ops}, kShapes_{ops}, "
+                    f"kTimes_{ops}}},\n")
+        f.write("};\n")
 
 
 if __name__ == "__main__":

@@ -249,6 +249,18 @@ const char *sgemm_mi355_config_name(int config);
 int sgemm_mi355_config_info(int config, int *bm, int *bn, int *bk, int *threads);
 
 /*
+ * Workgroups of configuration `config` that one compute unit of the current
+ * device holds at once (hipOccupancyMaxActiveBlocksPerMultiprocessor for the
+ * kernel the configuration runs on 16-byte aligned operands, at its
+ * workgroup size): writes it through `workgroups_per_cu`. Returns 0,
+ * SGEMM_MI355_ERR_CONFIG for an unknown id, SGEMM_MI355_ERR_NULL for a null
+ * pointer, or SGEMM_MI355_ERR_LAUNCH when the HIP runtime cannot answer (no
+ * device). Needs a GPU; enqueues nothing. The tuner records it next to its
+ * timings for the selection's model of partly filled waves.
+ */
+int sgemm_mi355_config_occupancy(int config, int *workgroups_per_cu);
+
+/*
  * Diagnostic: the workgroup -> C-tile map every kernel uses. For workgroup
  * `bid` of a tiles_m x tiles_n grid of block tiles walked in bands of
  * `group_m` tile rows, writes the tile row (*tm) and column (*tn). Workgroups
@@ -261,7 +273,7 @@ int sgemm_mi355_tile_map(int bid, int tiles_m, int tiles_n, int group_m, int *tm
 /* Static message for an error code (never NULL). */
 const char *sgemm_mi355_strerror(int code);
 
-/* Library version string, e.g. "0.4.0". */
+/* Library version string, e.g. "0.5.0". */
 const char *sgemm_mi355_version(void);
 
 #ifdef __cplusplus

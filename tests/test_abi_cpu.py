@@ -290,77 +290,153 @@ def test_select_splitk():
         sg.sgemm_mi355_select_splitk(2, 0, 1, 1, 1)
 
 
-def _table_entries():
-    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                        "dense_fp32_matrix_02_amd", "csrc", "tile_table.inc")
-    rows = re.findall(r'\{(\d+), (\d+), (\d+), "([^"]+)"\}', open(path).read())
-    return [(int(m), int(n), int(k), name) for m, n, k, name in rows]
+# ---- configuration selection, written out from its definition ---------------
+
+from tests._table import OP_PAIRS, read_table as _table  # noqa: E402
+
+SAT_CHAINS = 8         # resident 32x32 accumulator blocks per compute unit for full rate
+DIRECT = {(0, 0): "mfma32_256x256x16_w4x4_lds2", (1, 0): "mfma32_256x256x16_w4x4_lds2_tn",
+          (1, 1): "mfma32_256x256x16_w4x4_lds2_tt"}
 
 
-def test_table_lookup_matches_its_definition():
-    """The plain product's table lookup, written out here from its definition:
-    the entry of the same shape, else the nearest entry in log2 distance
-    among those within a factor of two in every dimension (first one on a
-    tie), else the rule (not covered here)."""
+_IDS = {}
+
+
+def _id(name):
+    if not _IDS:
+        _IDS.update({n: i for i, n in enumerate(sg.config_names())})
+    return _IDS[name]
+
+
+def _busy(cid, occ, M, N, K, batch=1):
+    """Busy time of the busiest compute unit: n = ceil(workgroups / 256)
+    workgroups, run occ at a time, stretched by SAT_CHAINS / resident
+    accumulator blocks while fewer are resident (a workgroup holds
+    k-groups * BM/32 * BN/32 blocks of 32x32), times ceil(K / BK)."""
     import math
-    import random
+    bm, bn, bk, _ = sg.sgemm_mi355_config_info(cid)
+    kg = re.search(r"_kg(\d+)", sg.sgemm_mi355_config_name(cid))
+    blocks = (int(kg.group(1)) if kg else 1) * (bm // 32) * (bn // 32)
+    wgs = math.ceil(M / bm) * math.ceil(N / bn) * min(batch, 65535)
+    n = math.ceil(wgs / 256)
+    resident = min(n, occ) * blocks
+    stretch = 1.0 if resident >= SAT_CHAINS else SAT_CHAINS / resident
+    return n * stretch * math.ceil(K / bk)
 
-    entries = _table_entries()
+
+def _direct_path(name, M, N, K):
+    """A direct-to-LDS configuration takes its direct path (aligned operands)."""
+    bk = sg.sgemm_mi355_config_info(_id(name))[2]
+    opA, opB = sg.sgemm_mi355_config_ops(_id(name))
+    return M > 0 and N > 0 and K > 0 and K % bk == 0 and (not opA or M % 4 == 0) and (opB or N % 4 == 0)
+
+
+def _model_select(blocks, opA, opB, M, N, K):
+    """The measured shape nearest (M, N, K) in summed |log2| distance among
+    those within a factor of two in each dimension (first on a tie), then the
+    candidate whose time there, scaled by the busy-time ratio, is least
+    (first on a tie); None when no measured shape qualifies."""
+    import math
+    cands, shapes, times = blocks[(opA, opB)]
+    near = None
+    for s, (m, n, k) in enumerate(shapes):
+        if M > 2 * m or m > 2 * M or N > 2 * n or n > 2 * N or K > 2 * k or k > 2 * K:
+            continue
+        d = abs(math.log2(M / m)) + abs(math.log2(N / n)) + abs(math.log2(K / k))
+        if near is None or d < near[0]:
+            near = (d, s)
+    if near is None:
+        return None
+    s = near[1]
+    m, n, k = shapes[s]
+    best = None
+    for c, (name, occ) in enumerate(cands):
+        t = times[s][c]
+        if t <= 0:
+            continue
+        if "_lds" in name and not _direct_path(name, M, N, K):
+            continue
+        cid = _id(name)
+        pred = t / _busy(cid, occ, m, n, k) * _busy(cid, occ, M, N, K)
+        if best is None or pred < best[0]:
+            best = (pred, name)
+    return best[1] if best else None
+
+
+def test_tile_table_is_consistent():
+    blocks = _table()
+    assert set(blocks) == set(OP_PAIRS.values())
+    names = set(sg.config_names())
+    for pair, (cands, shapes, times) in blocks.items():
+        assert 0 < len(cands) <= 64 and len(shapes) > 100
+        for name, occ in cands:
+            assert name in names and occ >= 1
+            assert sg.sgemm_mi355_config_ops(_id(name)) == pair
+        for s, row in enumerate(times):
+            assert all(t >= 0 for t in row) and max(row) > 0, (pair, shapes[s])
+            # the shape's best is stored, and nothing beyond 2x it (times have 5 significant digits)
+            b = min(t for t in row if t > 0)
+            assert all(t == 0 or t <= 2.0 * b * (1 + 1e-4) for t in row)
+        # every candidate is the fastest on at least one shape
+        winners = {cands[min((t, c) for c, t in enumerate(row) if t > 0)[1]][0] for row in times}
+        assert winners == {n for n, _ in cands}, pair
+
+
+def test_model_selection_matches_its_definition():
+    """Single products inside the measured range: the library's choice is the
+    model's, written out above, for every op pair."""
+    import random
+    blocks = _table()
     names = sg.config_names()
     rng = random.Random(7)
-    shapes = [(m, n, k) for m, n, k, _ in entries[:20]]
-    shapes += [(rng.randint(40, 20000), rng.randint(40, 20000), rng.randint(60, 40000)) for _ in range(400)]
     checked = 0
-    for M, N, K in shapes:
-        want = None
-        exact = [name for m, n, k, name in entries if (m, n, k) == (M, N, K)]
-        if exact:
-            want = exact[0]
-        else:
-            best = None
-            for m, n, k, name in entries:
-                d = [abs(math.log2(M / m)), abs(math.log2(N / n)), abs(math.log2(K / k))]
-                if max(d) > 1.0:
-                    continue
-                if best is None or sum(d) < best[0]:
-                    best = (sum(d), name)
-            want = best[1] if best else None
-        if want is None:
-            continue
-        if _direct_qualifies(M, N, K):
-            want = "mfma32_256x256x16_w4x4_lds2"
-        assert names[sg.sgemm_mi355_select_config(M, N, K)] == want, (M, N, K)
-        checked += 1
-    assert checked > 100
+    for (opA, opB), (_, shapes, _) in blocks.items():
+        cases = list(shapes[:30])
+        cases += [(rng.randint(64, 16384), rng.randint(64, 16384), rng.randint(128, 32768)) for _ in range(150)]
+        cases += [(3072, 3072, 4096), (6144, 6144, 1024), (8192, 8000, 4096), (1536, 1536, 4096), (8191, 8193, 8190)]
+        for M, N, K in cases:
+            want = _model_select(blocks, opA, opB, M, N, K)
+            got = names[sg.sgemm_mi355_select_config_ex(opA, opB, M, N, K, 1)]
+            if want is None:
+                continue
+            assert got == want, (opA, opB, M, N, K)
+            checked += 1
+    assert checked > 500
 
 
-def _direct_qualifies(M, N, K, batch=1):
-    """The switch to the direct-to-LDS 256x256x16 kernel, from its definition:
-    N a multiple of 256 and K of 16 (aligned operands assumed), at least 256
-    workgroups, at least 75% of the padded tile grid useful and at least 90%
-    of the last wave of 256 workgroups occupied."""
+def _direct_qualifies(opA, opB, M, N, K, batch=1):
+    """The rule's switch to the op pair's direct-to-LDS 256x256x16 kernel, from
+    its definition: the kernel's direct path (K a multiple of 16, M a multiple
+    of 4 for A^T, N a multiple of 4 for B), at least 256 workgroups, at least
+    75% of the padded tile grid useful and at least 90% of the last wave of
+    256 workgroups occupied. The transposed-B form has no direct kernel."""
     import math
-    if M <= 0 or K <= 0 or N % 256 or K % 16:
+    if (opA, opB) not in DIRECT or not _direct_path(DIRECT[(opA, opB)], M, N, K):
         return False
-    tiles = math.ceil(M / 256) * (N // 256)
+    tiles = math.ceil(M / 256) * math.ceil(N / 256)
     wgs = tiles * min(batch, 65535)
     fill = M * N / (tiles * 256 * 256)
     wave = wgs / (math.ceil(wgs / 256) * 256)
     return wgs >= 256 and fill >= 0.75 and wave >= 0.9
 
 
-def test_direct_kernel_switch_matches_its_definition():
+def test_rule_path_direct_switch_matches_its_definition():
+    """Batches, and single products with no measured shape within a factor of
+    two, take the rule, then the direct-kernel switch."""
     import random
     rng = random.Random(11)
     names = sg.config_names()
-    shapes = [(8192, 8192, 8192), (4096, 4096, 4096), (6144, 6144, 6144), (8000, 8000, 8000),
-              (4096, 4096, 4100), (1024, 8192, 1024), (300, 65536, 64)]
-    shapes += [(rng.randint(1, 12000), 256 * rng.randint(1, 48), 16 * rng.randint(1, 600)) for _ in range(300)]
-    for M, N, K in shapes:
-        got = names[sg.sgemm_mi355_select_config(M, N, K)]
-        assert (got == "mfma32_256x256x16_w4x4_lds2") == _direct_qualifies(M, N, K), (M, N, K, got)
-        for opA, opB in [(1, 0), (0, 1), (1, 1)]:  # the direct kernel is plain-only
-            assert "_lds" not in names[sg.sgemm_mi355_select_config_ex(opA, opB, M, N, K, 1)]
-    for M, N, K, batch in [(1024, 1024, 1024, 64), (512, 512, 64, 1000), (100, 256, 16, 3)]:
-        got = names[sg.sgemm_mi355_select_config_ex(0, 0, M, N, K, batch)]
-        assert (got == "mfma32_256x256x16_w4x4_lds2") == _direct_qualifies(M, N, K, batch), (M, N, K, batch)
+    blocks = _table()
+    cases = [(20000, 20000, 4096, 1), (32768, 4096, 1024, 1), (16640, 16640, 64, 1), (1024, 1024, 1024, 64),
+             (512, 512, 64, 1000), (100, 256, 16, 3), (2048, 2044, 512, 16), (4096, 4096, 4100, 2)]
+    cases += [(rng.randint(1, 12000), 4 * rng.randint(1, 3000), 16 * rng.randint(1, 600), rng.randint(2, 64))
+              for _ in range(200)]
+    cases += [(rng.randint(17000, 40000), rng.randint(1, 40000), rng.randint(1, 5000), 1) for _ in range(100)]
+    for M, N, K, batch in cases:
+        for opA, opB in OP_PAIRS.values():
+            if batch == 1 and _model_select(blocks, opA, opB, M, N, K) is not None:
+                continue
+            got = names[sg.sgemm_mi355_select_config_ex(opA, opB, M, N, K, batch)]
+            want = _direct_qualifies(opA, opB, M, N, K, batch)
+            assert (got == DIRECT.get((opA, opB))) == want, (opA, opB, M, N, K, batch, got)
+            assert ("_lds" in got) == want

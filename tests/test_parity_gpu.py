@@ -264,31 +264,38 @@ DIRECT_IDS = [i for i, n in enumerate(CONFIG_NAMES) if "_lds" in n]
 @pytest.mark.parametrize("cid", DIRECT_IDS, ids=[CONFIG_NAMES[i] for i in DIRECT_IDS])
 def test_direct_lds_configs_exact(cid):
     """Configurations that stage slabs with direct global-to-LDS loads take
-    that path only for 16-byte aligned operands with N a multiple of the tile
-    width and K a multiple of the slab depth: exercise it with ragged M and
-    slab counts that leave every remainder of the stage count, then a batch
-    and a split-K chunking, all exact on integer inputs."""
+    that path only for 16-byte aligned operands, K a multiple of the slab
+    depth and, for a line-contiguous operand (B, or A^T), its extent a
+    multiple of 4; lines past the edge of C are clamped. Exercise it with
+    ragged M and N (multiples of 4 and not), slab counts that leave every
+    remainder of the stage count, then a batch and a split-K chunking, all
+    exact on integer inputs, in the operand layouts the configuration reads."""
     bm, bn, bk, _ = sg.sgemm_mi355_config_info(cid)
+    opA, opB = sg.sgemm_mi355_config_ops(cid)
     seed = 500
-    for M in (1, bm - 1, bm + 3, 2 * bm):
-        for slabs in (1, 2, 3, 7, 32):
-            seed += 1
-            A, B = workloads.draw(M, 2 * bn, slabs * bk, seed, "int4")
-            C = _run_config(A, B, cid)
-            G.check_exact(C, np_(A), np_(B))
+    for M in (1, 4, bm - 1, bm + 4, 2 * bm):
+        for N in (2 * bn, bn + 36, 4, bn - 3):
+            for slabs in ((1, 2, 3, 7, 32) if N == 2 * bn else (1, 5)):
+                seed += 1
+                A, B = workloads.draw(M, N, slabs * bk, seed, "int4")
+                C = _run_config(A, B, cid)
+                G.check_exact(C, np_(A), np_(B))
     # strided batch of 3 entries (16-byte aligned strides)
-    batch, M, N, K = 3, bm + 5, bn, 9 * bk
-    A = torch.stack([workloads.draw(M, N, K, 700 + b, "int4")[0] for b in range(batch)])
-    B = torch.stack([workloads.draw(M, N, K, 800 + b, "int4")[1] for b in range(batch)])
+    batch, M, N, K = 3, bm + 4, bn + 12, 9 * bk
+    A = torch.stack([_stored(workloads.draw(M, N, K, 700 + b, "int4")[0], opA) for b in range(batch)])
+    B = torch.stack([_stored(workloads.draw(M, N, K, 800 + b, "int4")[1], opB) for b in range(batch)])
     print(f"[gpu] config={CONFIG_NAMES[cid]} batch={batch} M={M} N={N} K={K}", flush=True)
-    C = sg.gemm_strided_batched(G.dev(A), G.dev(B), config=cid)
+    C = sg.gemm_strided_batched(G.dev(A), G.dev(B), opA=opA, opB=opB, config=cid)
     torch.cuda.synchronize()
     for b in range(batch):
-        np.testing.assert_array_equal(C[b].cpu().numpy(), oracle.sgemm_f32(np_(A[b]), np_(B[b])))
+        Ab = np_(A[b]).T if opA else np_(A[b])
+        Bb = np_(B[b]).T if opB else np_(B[b])
+        np.testing.assert_array_equal(C[b].cpu().numpy(),
+                                      oracle.sgemm_f32(np.ascontiguousarray(Ab), np.ascontiguousarray(Bb)))
     # split-K: chunks of 32 slabs, the last one short but whole slabs
-    M, N, K = bm - 7, bn, 70 * bk
+    M, N, K = bm - 8, bn, 70 * bk
     A, B = workloads.draw(M, N, K, 900, "int4")
     print(f"[gpu] config={CONFIG_NAMES[cid]} split-K M={M} N={N} K={K}", flush=True)
-    Cs = sg.gemm_splitk(G.dev(A), G.dev(B), splits=3, config=cid)
+    Cs = sg.gemm_splitk(G.dev(_stored(A, opA)), G.dev(_stored(B, opB)), splits=3, opA=opA, opB=opB, config=cid)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(Cs.cpu().numpy(), oracle.sgemm_f32(np_(A), np_(B)))
