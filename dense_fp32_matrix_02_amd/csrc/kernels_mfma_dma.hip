@@ -189,9 +189,11 @@ struct DmaCfg {
 // DIRECT: every slab by direct loads (the launcher guarantees 16-byte aligned
 // chunks inside the matrices and K a multiple of BK); otherwise every slab
 // through registers. Two kernels rather than a branch, so each gets the
-// registers it needs.
+// registers it needs. The direct kernels are held to 128 VGPRs (four waves
+// per SIMD), so small tiles keep several workgroups per compute unit instead
+// of spending the register file on one.
 template <class Cfg, bool DIRECT>
-__global__ void __launch_bounds__(Cfg::NT) mfma_dma_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(Cfg::NT, DIRECT ? 4 : 1) mfma_dma_kernel(GemmArgs g) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int ST = Cfg::STAGES, NW = Cfg::NW;
   using SA = typename Cfg::SlabA;
@@ -422,6 +424,14 @@ KernelConfig kMfmaDmaConfigs[] = {
     // 256x256 block tile, 16 waves of 64x64, two stages: one workgroup per CU
     SGEMM_MFMA_DMA(256, 256, 16, 4, 4, 2),
     SGEMM_MFMA_DMA_OPS(256, 256, 16, 4, 4, 2),
+    // smaller tiles of 64x64 wave tiles, several workgroups per CU: mid-size
+    // shapes whose 256x256 grid leaves compute units idle or a last wave thin
+    SGEMM_MFMA_DMA(128, 128, 16, 2, 2, 2),
+    SGEMM_MFMA_DMA_OPS(128, 128, 16, 2, 2, 2),
+    SGEMM_MFMA_DMA(256, 128, 16, 4, 2, 2),
+    SGEMM_MFMA_DMA_OPS(256, 128, 16, 4, 2, 2),
+    SGEMM_MFMA_DMA(128, 256, 16, 2, 4, 2),
+    SGEMM_MFMA_DMA_OPS(128, 256, 16, 2, 4, 2),
 };
 const int kNumMfmaDmaConfigs = sizeof(kMfmaDmaConfigs) / sizeof(kMfmaDmaConfigs[0]);
 
