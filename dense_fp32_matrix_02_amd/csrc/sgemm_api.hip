@@ -34,8 +34,36 @@ struct TableBlock {
   const TableShape* shapes;
   const float* times_us;  // nshapes x ncand, row-major
 };
+struct SplitShape {
+  int M, N, K;
+  int splits;  // the fastest split count measured there
+};
 #include "tile_table.inc"
 constexpr int kNumTableBlocks = sizeof(kTableBlocks) / sizeof(kTableBlocks[0]);
+constexpr int kNumSplitShapes = sizeof(kSplitShapes) / sizeof(kSplitShapes[0]) - 1;  // without the sentinel
+
+// Index of the shape nearest (M, N, K) in (log M, log N, log K), summed
+// absolute distance, among those within a factor of two in every dimension
+// (the first on a tie); -1 when none qualifies.
+template <class Shape>
+int nearest_shape(const Shape* shapes, int count, int M, int N, int K) {
+  int near = -1;
+  double near_d = 1e30;
+  for (int s = 0; s < count; ++s) {
+    const Shape& e = shapes[s];
+    // within a factor of two in every dimension (integer test before any log)
+    if ((int64_t)M > 2LL * e.M || (int64_t)e.M > 2LL * M || (int64_t)N > 2LL * e.N ||
+        (int64_t)e.N > 2LL * N || (int64_t)K > 2LL * e.K || (int64_t)e.K > 2LL * K)
+      continue;
+    const double d = std::fabs(std::log2((double)M / e.M)) + std::fabs(std::log2((double)N / e.N)) +
+                     std::fabs(std::log2((double)K / e.K));
+    if (d < near_d) {
+      near_d = d;
+      near = s;
+    }
+  }
+  return near;
+}
 
 constexpr int kCompute = 256;  // compute units on MI355X
 
@@ -237,21 +265,7 @@ int model_select(int opA, int opB, int M, int N, int K, bool aligned) {
   const ResolvedBlock& rb = resolved().block[opA][opB];
   if (!rb.src) return -1;
   const TableBlock& tb = *rb.src;
-  int near = -1;
-  double near_d = 1e30;
-  for (int s = 0; s < tb.nshapes; ++s) {
-    const TableShape& e = tb.shapes[s];
-    // within a factor of two in every dimension (integer test before any log)
-    if ((int64_t)M > 2LL * e.M || (int64_t)e.M > 2LL * M || (int64_t)N > 2LL * e.N ||
-        (int64_t)e.N > 2LL * N || (int64_t)K > 2LL * e.K || (int64_t)e.K > 2LL * K)
-      continue;
-    const double d = std::fabs(std::log2((double)M / e.M)) + std::fabs(std::log2((double)N / e.N)) +
-                     std::fabs(std::log2((double)K / e.K));
-    if (d < near_d) {
-      near_d = d;
-      near = s;
-    }
-  }
+  const int near = nearest_shape(tb.shapes, tb.nshapes, M, N, K);
   if (near < 0) return -1;
   int best = -1;
   double best_t = 0.0;
@@ -485,20 +499,27 @@ int run_splitk(const Problem& p, float* C, int splits, float* W, size_t w_bytes,
   return SGEMM_MI355_OK;
 }
 
-// Split count and tile for a problem. Splitting pays only when the unsplit
-// grid leaves compute units idle or under-filled (fewer than two workgroups
-// per CU) and K is long enough that each chunk still does real work: then K
-// is cut into chunks of about kSplitChunk values of k (a power-of-two count).
-// Measured on the tuning shapes: 64x64x65536 and 128x128x16384 gain 5-10x,
-// 256x256x4096 1.8x, 512x512x8192 1.1x; at K <= 1024 the extra pass over C
-// costs more than it saves.
+// Split count and tile for a problem. Near the measured split-K grid (M, N
+// up to 2048 and K from 1024 to 65536, within a factor of two of a grid
+// shape in every dimension), the fastest split count measured at the
+// nearest grid shape: splitting pays where the tile grid leaves compute units
+// idle or a thin last wave, in proportion to K (on the grid, from 4 splits of
+// 64x64x1024 to 32 of 64x64x65536, none for 1024^2 at K <= 4096). Elsewhere a
+// rule: split only when the unsplit grid has fewer than two workgroups per CU,
+// into chunks of about kSplitChunk values of k (a power-of-two count). The
+// grid was measured for the plain product; the transposed forms use it too.
+// The chunk products take the rule's tile for the chunk shape.
 constexpr int kSplitChunk = 1024;
 
 void select_splitk(int opA, int opB, int M, int N, int K, int* splits, int* config) {
   const int single = select_mfma(opA, opB, M, N, K, 1);
   int s = 1;
-  if (tiles_for(*config_at(single), M, N) < 2 * kCompute)
+  const int near = (M > 0 && N > 0 && K > 0) ? nearest_shape(kSplitShapes, kNumSplitShapes, M, N, K) : -1;
+  if (near >= 0) {
+    s = kSplitShapes[near].splits;
+  } else if (tiles_for(*config_at(single), M, N) < 2 * kCompute) {
     while (2 * s <= kMaxSplits && (int64_t)K >= 2LL * s * kSplitChunk) s *= 2;
+  }
   const SplitPlan sp = plan_splits(K, s);
   *splits = sp.splits;
   *config = sp.splits == 1 ? single : rule_select(opA, opB, M, N, sp.kchunk, sp.splits);

@@ -49,7 +49,9 @@ TABLE_HEADER = """\
 // least one measured shape) with their occupancy (workgroups one compute
 // unit holds, from the HIP runtime), then per shape {{M, N, K}} and the
 // candidates' median times in microseconds; 0 marks a time more than
-// {cut}x the shape's best (never a candidate there).
+// {cut}x the shape's best (never a candidate there). A last block records,
+// per shape of a second grid, the fastest split count of sgemm_mi355_splitk,
+// which sgemm_mi355_select_splitk suggests for shapes near it.
 //
 // Written by dense_fp32_matrix_02_amd/tune.py (median of {reps} launches per
 // configuration and shape).
@@ -60,6 +62,10 @@ TABLE_HEADER = """\
 # against another by as much at a neighbouring shape.
 TABLE_CUT = 2.0
 OPS_NAMES = ("nn", "nt", "tn", "tt")
+# The split-K grid: shapes whose tile grids leave compute units idle, and K
+# long enough for splitting to be worth a second pass.
+SPLIT_SIDES = (64, 96, 128, 192, 256, 384, 512, 768, 1024, 1536, 2048, 3072)
+SPLIT_KS = (1024, 2048, 4096, 8192, 16384, 32768, 65536)
 
 
 def parse_shapes(text):
@@ -132,6 +138,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kinds", default="mfma", help="mfma, valu or mfma,valu")
     ap.add_argument("--splitk", default="", help="split counts to time with sgemm_mi355_splitk, e.g. 2,4,8")
+    ap.add_argument("--splitk-grid", action="store_true",
+                    help="time split counts 1..64 on the grid M, N in {64..3072} (powers of two and 1.5x them) x K in {1024..65536} "
+                         "(powers of two) for the table's split-K block (no per-configuration timings)")
     ap.add_argument("--json", default=None)
     ap.add_argument("--table", default=None)
     ap.add_argument("--from-json", default=None, metavar="JSON",
@@ -145,6 +154,12 @@ def main(argv=None):
     if args.splitk and (opA or opB or args.batch != 1):
         ap.error("--splitk times plain single products")
 
+    if args.splitk_grid:
+        if opA or opB or args.batch != 1 or args.grid:
+            ap.error("--splitk-grid times plain single products on its own grid")
+        args.kinds = "none"
+        args.splitk = "1,2,4,8,16,32,64"
+        args.shapes = ",".join(f"{m}x{n}x{k}" for m in SPLIT_SIDES for n in SPLIT_SIDES for k in SPLIT_KS)
     if args.from_json:
         results = []
         for path in args.from_json.split(","):
@@ -244,6 +259,14 @@ def write_table(results, path, reps):
                 f.write("    " + ", ".join(cells) + ",\n")
             f.write("};\n")
             blocks.append((ops, len(cands), len(rows)))
+        split_rows = [r for r in results if r.get("splitk_ms") and r.get("batch", 1) == 1
+                      and r.get("ops", "nn") == "nn"]
+        f.write("\n// split-K: per measured shape {M, N, K, fastest split count} among 1, 2, 4, ..., 64\n")
+        f.write("static const SplitShape kSplitShapes[] = {\n")
+        for r in split_rows:
+            t = {int(k): v for k, v in r["splitk_ms"].items()}
+            f.write(f'    {{{r["M"]}, {r["N"]}, {r["K"]}, {min(t, key=t.get)}}},\n')
+        f.write("    {0, 0, 0, 0},  // sentinel\n};\n")
         f.write("\nstatic const TableBlock kTableBlocks[] = {\n")
         for ops, nc, nr in blocks:
             f.write(f"    {{{int(ops[0] == 't')}, {int(ops[1] == 't')}, {nc}, {nr}, kCand_{ops}, kShapes_{ops}, "

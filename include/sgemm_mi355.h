@@ -189,11 +189,16 @@ int sgemm_mi355_splitk_with_config(int opA, int opB, int M, int N, int K, float 
 
 /*
  * Split count and tile configuration the library suggests for a problem
- * (host only): no split while the unsplit tile grid gives at least two
- * workgroups per compute unit; otherwise the largest power of two that keeps
- * chunks of at least 1024 values of k (so K < 2048 is never split). Writes
- * *splits and *config (the configuration of the chunk products, or of the
- * whole product when *splits is 1).
+ * (host only). Within a factor of two (in each of M, N, K) of the measured
+ * split-K grid (M, N from 64 to 2048, K from 1024 to 65536, powers of two),
+ * the fastest split count measured at the nearest grid shape. Elsewhere: no
+ * split while the unsplit tile grid gives at least two workgroups per compute
+ * unit, otherwise the largest power of two that keeps chunks of at least 1024
+ * values of k. The count is then cut into chunks as sgemm_mi355_splitk does
+ * (multiples of 32 values of k). Writes *splits and *config (the
+ * configuration of the chunk products, or of the whole product when *splits
+ * is 1). Returns 0, or SGEMM_MI355_ERR_OP / SGEMM_MI355_ERR_DIM / _NULL for
+ * bad arguments.
  */
 int sgemm_mi355_select_splitk(int opA, int opB, int M, int N, int K, int *splits, int *config);
 

@@ -32,3 +32,27 @@ def read_table(path: str = TABLE_PATH):
         times = [cells[i * len(cands):(i + 1) * len(cands)] for i in range(len(shapes))]
         blocks[pair] = (cands, shapes, times)
     return blocks
+
+
+def read_split_table(path: str = TABLE_PATH):
+    """The split-K block: [(M, N, K, fastest split count)] in table order."""
+    text = open(path).read()
+    body = re.search(r"kSplitShapes\[\] = \{(.*?)\n\};", text, re.S).group(1)
+    rows = [tuple(int(x) for x in t) for t in re.findall(r"\{(\d+), (\d+), (\d+), (\d+)\}", body)]
+    return [r for r in rows if r[0] > 0]  # without the sentinel
+
+
+def nearest(shapes, M, N, K):
+    """Index of the shape (first three fields M, N, K) nearest (M, N, K) in
+    summed |log2| distance among those within a factor of two in every
+    dimension (the first on a tie), or None."""
+    import math
+    near = None
+    for i, e in enumerate(shapes):
+        m, n, k = e[0], e[1], e[2]
+        if M > 2 * m or m > 2 * M or N > 2 * n or n > 2 * N or K > 2 * k or k > 2 * K:
+            continue
+        d = abs(math.log2(M / m)) + abs(math.log2(N / n)) + abs(math.log2(K / k))
+        if near is None or d < near[0]:
+            near = (d, i)
+    return None if near is None else near[1]

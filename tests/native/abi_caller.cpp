@@ -125,6 +125,23 @@ int main() {
     ref_sgemm_ex_f32(1, 0, M, N, K, 2.0f, A.data(), lda, B.data(), ldb, -1.0f, want.data(), ldc);
     check("sgemm_mi355_ex tn alpha=2 beta=-1", rc, dC.get(), want);
   }
+  {  // both operands transposed through a direct global-to-LDS configuration, forced by name
+    const int M = 300, N = 260, K = 160, lda = M, ldb = K, ldc = N;
+    int cid = -1;
+    for (int i = 0; i < sgemm_mi355_num_configs(); ++i)
+      if (std::strcmp(sgemm_mi355_config_name(i), "mfma32_256x256x16_w4x4_lds2_tt") == 0) cid = i;
+    Ints g(5);
+    std::vector<float> A = g.fill((size_t)K * lda), B = g.fill((size_t)N * ldb);
+    std::vector<float> C0((size_t)M * ldc, nan), want = C0;
+    Dev dA(A), dB(B), dC(C0);
+    const int rc = cid < 0 ? SGEMM_MI355_ERR_CONFIG
+                           : sgemm_mi355_strided_batched_with_config(SGEMM_MI355_OP_T, SGEMM_MI355_OP_T, M, N, K, 1.0f,
+                                                                     dA.p, lda, 0, dB.p, ldb, 0, 0.0f, dC.p, ldc,
+                                                                     0, 1, stream, cid);
+    HIP_OK(hipStreamSynchronize(stream));
+    ref_sgemm_ex_f32(1, 1, M, N, K, 1.0f, A.data(), lda, B.data(), ldb, 0.0f, want.data(), ldc);
+    check("direct-LDS tt configuration 300x260x160", rc, dC.get(), want);
+  }
   {  // strided batch with a shared B (strideB = 0)
     const int batch = 5, M = 70, N = 45, K = 33;
     Ints g(3);

@@ -234,6 +234,22 @@ def test_select_config_ex_matches_ops():
     assert sg.sgemm_mi355_config_info(big)[0] >= sg.sgemm_mi355_config_info(small)[0]
 
 
+def test_config_occupancy_errors_and_values():
+    """Unknown ids and null outputs are rejected before any HIP call. Without
+    a device the runtime query reports a launch error; with one, every
+    configuration holds at least one workgroup per compute unit."""
+    import ctypes
+    lib = sg.load()
+    n = ctypes.c_int(-1)
+    assert lib.sgemm_mi355_config_occupancy(-1, ctypes.byref(n)) == sg.ERR_CONFIG
+    assert lib.sgemm_mi355_config_occupancy(sg.sgemm_mi355_num_configs(), ctypes.byref(n)) == sg.ERR_CONFIG
+    assert lib.sgemm_mi355_config_occupancy(0, None) == sg.ERR_NULL
+    rc = lib.sgemm_mi355_config_occupancy(0, ctypes.byref(n))
+    assert rc in (sg.OK, sg.ERR_LAUNCH)
+    if rc == sg.OK:
+        assert n.value >= 1
+
+
 def test_binding_leading_dimension_of_torch_tensors():
     """Row stride read from torch tensors: padded rows keep their stride, and
     a size-1 dimension's stride (arbitrary in torch) is ignored."""
@@ -274,18 +290,54 @@ def test_splitk_rejects_bad_arguments_before_any_hip_call():
     assert f(0, 0, 100, 50, 1000, 1.0, A0, 1000, B0, 50, 0.0, C0, 50, 4, A0 + 4000, need, 0) == sg.ERR_ALIAS
 
 
-def test_select_splitk():
-    for opA, opB in [(0, 0), (1, 1)]:
-        sp, cid = sg.sgemm_mi355_select_splitk(opA, opB, 8192, 8192, 8192)
-        assert sp == 1 and sg.sgemm_mi355_config_ops(cid) == (opA, opB)
-        sp, cid = sg.sgemm_mi355_select_splitk(opA, opB, 256, 256, 8192)
-        assert sp > 1 and sg.sgemm_mi355_config_ops(cid) == (opA, opB)
-    sp, _ = sg.sgemm_mi355_select_splitk(0, 0, 256, 256, 2047)
-    assert sp == 1                                    # chunks would be shorter than 1024
-    sp, _ = sg.sgemm_mi355_select_splitk(0, 0, 64, 64, 65536)
-    assert sp == 64                                   # K / 1024 chunks
-    sp, _ = sg.sgemm_mi355_select_splitk(0, 0, 1024, 1024, 1024)
-    assert sp == 1
+def _plan_splits(K, s):
+    """Effective split count: chunks of ceil(K/s) rounded up to 32."""
+    s = max(s, 1)
+    if K <= 0:
+        return 1
+    kc = -(-K // s)
+    kc = -(-kc // 32) * 32
+    eff = -(-K // kc)
+    return 1 if eff <= 1 else eff
+
+
+def _rule_splits(opA, opB, M, N, K):
+    """Outside the measured split-K grid: split only when the unsplit grid has
+    fewer than 512 workgroups, into the largest power-of-two count whose
+    chunks keep at least 1024 values of k."""
+    import math
+    bm, bn, _, _ = sg.sgemm_mi355_config_info(sg.sgemm_mi355_select_config_ex(opA, opB, M, N, K, 1))
+    s = 1
+    if math.ceil(M / bm) * math.ceil(N / bn) < 512:
+        while 2 * s <= 256 and K >= 2 * s * 1024:
+            s *= 2
+    return _plan_splits(K, s)
+
+
+def test_select_splitk_matches_its_definition():
+    """Near the measured split-K grid: the fastest split count at the nearest
+    grid shape (then chunked as the entry point does); elsewhere the rule."""
+    import random
+    from tests._table import nearest, read_split_table
+    table = read_split_table()
+    assert len(table) > 200 and all(s in (1, 2, 4, 8, 16, 32, 64) for *_, s in table)
+    rng = random.Random(5)
+    cases = [(m, n, k) for m, n, k, _ in table[::7]]
+    cases += [(rng.randint(1, 5000), rng.randint(1, 5000), rng.randint(1, 140000)) for _ in range(300)]
+    cases += [(rng.randint(6200, 30000), rng.randint(1, 30000), rng.randint(1, 140000)) for _ in range(80)]
+    cases += [(8192, 8192, 8192), (768, 768, 65536), (3000, 100, 100000), (33, 47, 1_000_003), (1, 1, 1)]
+    near_seen = rule_seen = 0
+    for M, N, K in cases:
+        near = nearest(table, M, N, K)
+        for opA, opB in [(0, 0), (1, 1)]:
+            want = _plan_splits(K, table[near][3]) if near is not None else _rule_splits(opA, opB, M, N, K)
+            sp, cid = sg.sgemm_mi355_select_splitk(opA, opB, M, N, K)
+            assert sp == want, (opA, opB, M, N, K)
+            assert sg.sgemm_mi355_config_ops(cid) == (opA, opB)
+        near_seen += near is not None
+        rule_seen += near is None
+    assert near_seen > 100 and rule_seen > 50
+    assert sg.sgemm_mi355_select_splitk(0, 0, 8192, 8192, 8192)[0] == 1   # fills the chip: no split
     with pytest.raises(sg.SgemmError):
         sg.sgemm_mi355_select_splitk(2, 0, 1, 1, 1)
 
