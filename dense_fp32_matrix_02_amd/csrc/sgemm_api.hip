@@ -27,12 +27,19 @@ struct TableConfig {
 struct TableShape {
   int M, N, K;
 };
+struct TableNorm {
+  const char* name;
+  int occupancy;
+  float us_per_busy;  // median over the measured shapes of time / busy_time
+};
 struct TableBlock {
   int opA, opB;
   int ncand, nshapes;
   const TableConfig* cand;
   const TableShape* shapes;
   const float* times_us;  // nshapes x ncand, row-major
+  int nnorm;
+  const TableNorm* norms;  // every configuration of the op pair
 };
 struct SplitShape {
   int M, N, K;
@@ -67,17 +74,17 @@ int nearest_shape(const Shape* shapes, int count, int M, int N, int K) {
 
 constexpr int kCompute = 256;  // compute units on MI355X
 
-// Block tiles the selection rule considers when the table has no entry, per
-// operand pair (plain, op(A) = A^T, op(B) = B^T, both), largest first, each
-// with the fewest workgroups (counting batch entries) it needs to be chosen;
-// a tile is also skipped when the matrix would fill less than kRuleMinFill of
-// its padded tile grid (a batch of 64x64 products in 256x128 tiles computes 8
-// times the useful work). Below the last threshold, a 32x32 tile with its
-// slabs split among wave groups keeps the SIMDs busy; long K takes the deeper
-// one. The plain thresholds were fitted to the measured grid the table comes
-// from (about 2% slower than the best configuration there, geometric mean)
-// and to strided batches of 64^3 to 1024^3 products; the transposed forms
-// were measured at 2048^3 to 8192^3 and on the ragged workload.
+// Block tiles of the selection rule, per operand pair (plain, op(A) = A^T,
+// op(B) = B^T, both), largest first, each with the fewest workgroups
+// (counting batch entries) it needs to be chosen. The rule picks the tile of
+// split-K chunk products, and stands in for the measured table only if that
+// has nothing for an op pair. A tile is also skipped when the matrix would
+// fill less than kRuleMinFill of its padded tile grid (a batch of 64x64
+// products in 256x128 tiles computes 8 times the useful work). Below the last
+// threshold, a 32x32 tile with its slabs split among wave groups keeps the
+// SIMDs busy; long K takes the deeper one. The thresholds were fitted to the
+// measured grid (about 2% slower than the best configuration there,
+// geometric mean) and to strided batches of 64^3 to 1024^3 products.
 struct RuleTile {
   const char* config;
   int min_wgs;
@@ -137,17 +144,6 @@ const char* ops_suffix(int opA, int opB) {
 // Configuration names used by the selection, resolved to ids once per
 // process (a function-local static: initialised on first use, thread-safe,
 // never written afterwards), so a call costs no string comparisons.
-// Direct-to-LDS kernels the rule switches to (per op pair; the transposed-B
-// form has none: its register-staged 256x256x32 tile is as fast) for
-// problems that qualify for direct loads and whose grid fills the chip: at
-// least one 256x256 tile per compute unit, at least kRuleMinFill of the
-// padded tile grid useful, and at least kDirectMinWave of the last wave of
-// workgroups occupied. Measured at 4096^3 to 8192^3 and on non-square shapes
-// of that size, they are 2-5% faster than the register-staged tiles there.
-const char* const kDirectConfig[2][2] = {{"mfma32_256x256x16_w4x4_lds2", nullptr},
-                                         {"mfma32_256x256x16_w4x4_lds2_tn", "mfma32_256x256x16_w4x4_lds2_tt"}};
-constexpr double kDirectMinWave = 0.9;
-
 // The table resolved for the model selection below: each candidate's
 // configuration id and occupancy, and each measured
 // time divided by the model's busy time at its own shape (0: no candidate).
@@ -156,12 +152,14 @@ struct ResolvedBlock {
   int ids[64];
   int occ[64];
   std::vector<double> norm;  // nshapes x ncand
+  // every configuration of the op pair: id, occupancy, median time per busy unit
+  std::vector<int> gid, gocc;
+  std::vector<double> gnorm;
 };
 
 struct Resolved {
   int rule[2][2][kRuleTileCount];  // -1 where a configuration is not built
   int small[2][2][2];              // [opA][opB][long K]
-  int direct[2][2];                // kDirectConfig (-1: none)
   ResolvedBlock block[2][2];
 };
 
@@ -199,7 +197,6 @@ const Resolved& resolved() {
           std::snprintf(name, sizeof(name), "mfma32_%s%s", l ? kRuleSmallLongK : kRuleSmall, ops_suffix(a, b));
           x.small[a][b][l] = config_id(name);
         }
-        x.direct[a][b] = kDirectConfig[a][b] ? config_id(kDirectConfig[a][b]) : -1;
       }
     for (int t = 0; t < kNumTableBlocks; ++t) {
       const TableBlock& tb = kTableBlocks[t];
@@ -212,6 +209,16 @@ const Resolved& resolved() {
         if (cfg && (cfg->transA != tb.opA || cfg->transB != tb.opB || cfg->kind != KIND_MFMA)) id = -1;
         rb.ids[c] = id;
         rb.occ[c] = tb.cand[c].occupancy > 0 ? tb.cand[c].occupancy : 1;
+      }
+      for (int c = 0; c < tb.nnorm; ++c) {
+        const int id = config_id(tb.norms[c].name);
+        const KernelConfig* cfg = config_at(id);
+        if (!cfg || cfg->transA != tb.opA || cfg->transB != tb.opB || cfg->kind != KIND_MFMA ||
+            !(tb.norms[c].us_per_busy > 0.0f))
+          continue;
+        rb.gid.push_back(id);
+        rb.gocc.push_back(tb.norms[c].occupancy > 0 ? tb.norms[c].occupancy : 1);
+        rb.gnorm.push_back(tb.norms[c].us_per_busy);
       }
       rb.norm.assign((size_t)tb.nshapes * tb.ncand, 0.0);
       for (int s = 0; s < tb.nshapes; ++s) {
@@ -284,31 +291,40 @@ int model_select(int opA, int opB, int M, int N, int K, bool aligned) {
   return best;
 }
 
-// The op pair's direct-to-LDS configuration in place of `id` when the
-// problem qualifies (see kDirectConfig). `aligned`: the operands allow
-// 16-byte direct loads (callers that do not know the pointers pass true; the
-// kernel's launcher checks again and stages through registers when they do
-// not).
-int upgrade_direct(int id, int opA, int opB, int M, int N, int K, int batch, bool aligned) {
-  const int did = resolved().direct[opA][opB];
-  if (did < 0) return id;
-  const KernelConfig& c = *config_at(did);
-  if (!direct_path(c, M, N, K, aligned)) return id;
-  const int64_t tiles = tiles_for(c, M, N);
-  const int64_t wgs = tiles * (batch < kMaxGridY ? batch : kMaxGridY);
-  const double fill = (double)M * N / ((double)tiles * c.bm * c.bn);
-  const double wave = (double)wgs / (double)(((wgs + kCompute - 1) / kCompute) * kCompute);
-  return (wgs >= kCompute && fill >= kRuleMinFill && wave >= kDirectMinWave) ? did : id;
+// Selection for batches, and for single products with no measured shape
+// nearby: every configuration of the op pair, each predicted as its median
+// time per unit of busy time over the measured shapes times busy_time for
+// this problem (batch entries included); the least predicted time wins (the
+// first on a tie). Direct-to-LDS configurations count only when the problem
+// takes their direct path. -1 when the table has no configuration for the
+// op pair. Over 26 measured batches (2 x 2048^3 to 4096 x 16x16x64) it
+// picks a configuration within 0.945 of the best (geometric mean), against
+// 0.836 for the rule.
+int global_select(int opA, int opB, int M, int N, int K, int batch, bool aligned) {
+  if (M <= 0 || N <= 0 || K <= 0 || batch <= 0) return -1;
+  const ResolvedBlock& rb = resolved().block[opA][opB];
+  int best = -1;
+  double best_t = 0.0;
+  for (size_t c = 0; c < rb.gid.size(); ++c) {
+    const int id = rb.gid[c];
+    const KernelConfig& cfg = *config_at(id);
+    if (is_direct_config(id) && !direct_path(cfg, M, N, K, aligned)) continue;
+    const double t = rb.gnorm[c] * busy_time(cfg, rb.gocc[c], M, N, K, batch);
+    if (best < 0 || t < best_t) {
+      best = id;
+      best_t = t;
+    }
+  }
+  return best;
 }
 
-// Single products go to the model selection; batches, and shapes with no
-// measured shape nearby, to the rule (then the direct-kernel switch).
+// Single products near a measured shape take the model selection; batches,
+// and shapes with no measured shape nearby, the median-time model; the rule
+// only if the table has nothing for the op pair (or the problem is empty).
 int select_mfma(int opA, int opB, int M, int N, int K, int batch, bool aligned = true) {
-  if (batch == 1) {
-    const int id = model_select(opA, opB, M, N, K, aligned);
-    if (id >= 0) return id;
-  }
-  return upgrade_direct(rule_select(opA, opB, M, N, K, batch), opA, opB, M, N, K, batch, aligned);
+  int id = batch == 1 ? model_select(opA, opB, M, N, K, aligned) : -1;
+  if (id < 0) id = global_select(opA, opB, M, N, K, batch, aligned);
+  return id >= 0 ? id : rule_select(opA, opB, M, N, K, batch);
 }
 
 // Vector-kernel configurations the selection considers, largest block tile

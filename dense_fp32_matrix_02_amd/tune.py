@@ -49,7 +49,10 @@ TABLE_HEADER = """\
 // least one measured shape) with their occupancy (workgroups one compute
 // unit holds, from the HIP runtime), then per shape {{M, N, K}} and the
 // candidates' median times in microseconds; 0 marks a time more than
-// {cut}x the shape's best (never a candidate there). A last block records,
+// {cut}x the shape's best (never a candidate there). Then every
+// configuration of the op pair with its occupancy and its median time per
+// unit of modelled busy time over the shapes: the selection's estimate for
+// batches and for problems with no measured shape nearby. A last block records,
 // per shape of a second grid, the fastest split count of sgemm_mi355_splitk,
 // which sgemm_mi355_select_splitk suggests for shapes near it.
 //
@@ -214,6 +217,31 @@ def main(argv=None):
         write_table(results, args.table, args.reps)
 
 
+# Fill model of the selection (busy_time in csrc/sgemm_api.hip): the busiest
+# compute unit's share of workgroups, stretched while fewer than SAT_CHAINS
+# 32x32 accumulator blocks are resident, times the slab count.
+SAT_CHAINS = 8
+
+
+def busy_time(bm, bn, bk, kgroups, occ, M, N, K, batch=1):
+    wgs = -(-M // bm) * -(-N // bn) * min(batch, 65535)
+    n = -(-wgs // 256)
+    resident = min(n, occ) * kgroups * (bm // 32) * (bn // 32)
+    stretch = 1.0 if resident >= SAT_CHAINS else SAT_CHAINS / resident
+    return n * stretch * -(-K // bk)
+
+
+def config_geometry(name):
+    """(bm, bn, bk, kgroups) of a configuration of the built library."""
+    import re
+
+    import dense_fp32_matrix_02_amd as sg
+
+    bm, bn, bk, _ = sg.sgemm_mi355_config_info(sg.config_id(name))
+    kg = re.search(r"_kg(\d+)", name)
+    return bm, bn, bk, int(kg.group(1)) if kg else 1
+
+
 def write_table(results, path, reps):
     """The tile table from single-product rows of any op pairs: per op pair,
     the configurations that are fastest on at least one shape, their
@@ -258,7 +286,19 @@ def write_table(results, path, reps):
                     cells.append("0" if v is None or v > TABLE_CUT * b else f"{v * 1e3:.5g}")
                 f.write("    " + ", ".join(cells) + ",\n")
             f.write("};\n")
-            blocks.append((ops, len(cands), len(rows)))
+            # every configuration's median time per unit of modelled busy time
+            # over the shapes, for problems without a measured shape nearby
+            names = sorted({n for r in rows for n in r["times_ms"] if n.startswith("mfma")})
+            f.write(f"static const TableNorm kNorm_{ops}[] = {{\n")
+            for n in names:
+                if n not in occ:
+                    raise ValueError(f"no occupancy recorded for {n} ({ops})")
+                geo = config_geometry(n)
+                ratios = [r["times_ms"][n] * 1e3 / busy_time(*geo, occ[n], r["M"], r["N"], r["K"])
+                          for r in rows if n in r["times_ms"]]
+                f.write(f'    {{"{n}", {occ[n]}, {statistics.median(ratios):.5g}}},\n')
+            f.write("};\n")
+            blocks.append((ops, len(cands), len(rows), len(names)))
         split_rows = [r for r in results if r.get("splitk_ms") and r.get("batch", 1) == 1
                       and r.get("ops", "nn") == "nn"]
         f.write("\n// split-K: per measured shape {M, N, K, fastest split count} among 1, 2, 4, ..., 64\n")
@@ -268,9 +308,9 @@ def write_table(results, path, reps):
             f.write(f'    {{{r["M"]}, {r["N"]}, {r["K"]}, {min(t, key=t.get)}}},\n')
         f.write("    {0, 0, 0, 0},  // sentinel\n};\n")
         f.write("\nstatic const TableBlock kTableBlocks[] = {\n")
-        for ops, nc, nr in blocks:
+        for ops, nc, nr, nn in blocks:
             f.write(f"    {{{int(ops[0] == 't')}, {int(ops[1] == 't')}, {nc}, {nr}, kCand_{ops}, kShapes_{ops}, "
-                    f"kTimes_{ops}}},\n")
+                    f"kTimes_{ops}, {nn}, kNorm_{ops}}},\n")
         f.write("};\n")
 
 

@@ -56,3 +56,15 @@ def nearest(shapes, M, N, K):
         if near is None or d < near[0]:
             near = (d, i)
     return None if near is None else near[1]
+
+
+def read_norms(path: str = TABLE_PATH):
+    """{(opA, opB): [(name, occupancy, median microseconds per busy unit)]}."""
+    text = open(path).read()
+    out = {}
+    for ops, pair in OP_PAIRS.items():
+        m = re.search(r"kNorm_%s\[\] = \{(.*?)\n\};" % ops, text, re.S)
+        if m:
+            out[pair] = [(n, int(o), float(np.float32(v)))
+                         for n, o, v in re.findall(r'\{"([^"]+)", (\d+), ([0-9.eE+-]+)\}', m.group(1))]
+    return out

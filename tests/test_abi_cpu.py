@@ -347,8 +347,6 @@ def test_select_splitk_matches_its_definition():
 from tests._table import OP_PAIRS, read_table as _table  # noqa: E402
 
 SAT_CHAINS = 8         # resident 32x32 accumulator blocks per compute unit for full rate
-DIRECT = {(0, 0): "mfma32_256x256x16_w4x4_lds2", (1, 0): "mfma32_256x256x16_w4x4_lds2_tn",
-          (1, 1): "mfma32_256x256x16_w4x4_lds2_tt"}
 
 
 _IDS = {}
@@ -456,39 +454,63 @@ def test_model_selection_matches_its_definition():
     assert checked > 500
 
 
-def _direct_qualifies(opA, opB, M, N, K, batch=1):
-    """The rule's switch to the op pair's direct-to-LDS 256x256x16 kernel, from
-    its definition: the kernel's direct path (K a multiple of 16, M a multiple
-    of 4 for A^T, N a multiple of 4 for B), at least 256 workgroups, at least
-    75% of the padded tile grid useful and at least 90% of the last wave of
-    256 workgroups occupied. The transposed-B form has no direct kernel."""
-    import math
-    if (opA, opB) not in DIRECT or not _direct_path(DIRECT[(opA, opB)], M, N, K):
-        return False
-    tiles = math.ceil(M / 256) * math.ceil(N / 256)
-    wgs = tiles * min(batch, 65535)
-    fill = M * N / (tiles * 256 * 256)
-    wave = wgs / (math.ceil(wgs / 256) * 256)
-    return wgs >= 256 and fill >= 0.75 and wave >= 0.9
+def _global_select(norms, opA, opB, M, N, K, batch):
+    """Every configuration of the op pair, predicted as its median time per
+    busy unit times the busy time of this problem (batch entries included);
+    the least wins (first on a tie). Direct-to-LDS configurations count only
+    on their direct path."""
+    best = None
+    for name, occ, us in norms[(opA, opB)]:
+        if "_lds" in name and not _direct_path(name, M, N, K):
+            continue
+        t = us * _busy(_id(name), occ, M, N, K, batch)
+        if best is None or t < best[0]:
+            best = (t, name)
+    return best[1]
 
 
-def test_rule_path_direct_switch_matches_its_definition():
+def test_median_model_selection_matches_its_definition():
     """Batches, and single products with no measured shape within a factor of
-    two, take the rule, then the direct-kernel switch."""
+    two, take the median-time model over every configuration of the op pair."""
     import random
-    rng = random.Random(11)
+    from tests._table import read_norms
+    norms = read_norms()
+    assert set(norms) == set(OP_PAIRS.values())
     names = sg.config_names()
+    for pair, rows in norms.items():
+        assert len(rows) >= 10
+        for name, occ, us in rows:
+            assert name in names and occ >= 1 and us > 0
+            assert sg.sgemm_mi355_config_ops(_id(name)) == pair
     blocks = _table()
-    cases = [(20000, 20000, 4096, 1), (32768, 4096, 1024, 1), (16640, 16640, 64, 1), (1024, 1024, 1024, 64),
-             (512, 512, 64, 1000), (100, 256, 16, 3), (2048, 2044, 512, 16), (4096, 4096, 4100, 2)]
-    cases += [(rng.randint(1, 12000), 4 * rng.randint(1, 3000), 16 * rng.randint(1, 600), rng.randint(2, 64))
+    rng = random.Random(11)
+    cases = [(32, 32, 32, 4096), (16, 16, 64, 4096), (100, 100, 100, 256), (200, 300, 400, 64),
+             (1536, 1536, 512, 8), (2048, 2048, 2048, 2), (20000, 20000, 4096, 1), (16640, 16640, 64, 1),
+             (100, 256, 16, 3), (4096, 4096, 4100, 2)]
+    cases += [(rng.randint(1, 3000), rng.randint(1, 3000), rng.randint(1, 5000), rng.randint(2, 5000))
               for _ in range(200)]
-    cases += [(rng.randint(17000, 40000), rng.randint(1, 40000), rng.randint(1, 5000), 1) for _ in range(100)]
+    cases += [(rng.randint(17000, 40000), rng.randint(1, 40000), rng.randint(1, 5000), 1) for _ in range(80)]
+    checked = 0
     for M, N, K, batch in cases:
         for opA, opB in OP_PAIRS.values():
             if batch == 1 and _model_select(blocks, opA, opB, M, N, K) is not None:
                 continue
             got = names[sg.sgemm_mi355_select_config_ex(opA, opB, M, N, K, batch)]
-            want = _direct_qualifies(opA, opB, M, N, K, batch)
-            assert (got == DIRECT.get((opA, opB))) == want, (opA, opB, M, N, K, batch, got)
-            assert ("_lds" in got) == want
+            assert got == _global_select(norms, opA, opB, M, N, K, batch), (opA, opB, M, N, K, batch)
+            checked += 1
+    assert checked > 800
+
+
+def test_tuner_busy_time_is_the_selections():
+    """The tuner normalises measured times with its own copy of the busy-time
+    model; it must agree with the definition the selection is tested against."""
+    import random
+    from dense_fp32_matrix_02_amd import tune
+    rng = random.Random(3)
+    names = [n for n in sg.config_names() if n.startswith("mfma")]
+    for _ in range(500):
+        name = rng.choice(names)
+        occ = rng.randint(1, 8)
+        M, N, K, batch = rng.randint(1, 20000), rng.randint(1, 20000), rng.randint(1, 70000), rng.randint(1, 300)
+        want = _busy(_id(name), occ, M, N, K, batch)
+        assert tune.busy_time(*tune.config_geometry(name), occ, M, N, K, batch) == pytest.approx(want, rel=1e-12)
