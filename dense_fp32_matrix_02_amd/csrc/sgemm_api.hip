@@ -141,12 +141,12 @@ const char* ops_suffix(int opA, int opB) {
   return s[opA][opB];
 }
 
-// Configuration names used by the selection, resolved to ids once per
-// process (a function-local static: initialised on first use, thread-safe,
-// never written afterwards), so a call costs no string comparisons.
-// The table resolved for the model selection below: each candidate's
-// configuration id and occupancy, and each measured
-// time divided by the model's busy time at its own shape (0: no candidate).
+// The selection's data, resolved once per process (a function-local static:
+// initialised on first use, thread-safe, never written afterwards), so a call
+// costs no string comparisons: the rule's configuration ids and, per op pair,
+// the table's candidates (id, occupancy, and each measured time divided by
+// the busy time at its own shape, 0 where not a candidate) and every
+// configuration's id, occupancy and median time per busy unit.
 struct ResolvedBlock {
   const TableBlock* src = nullptr;
   int ids[64];
@@ -180,6 +180,7 @@ constexpr int kSatChains = 8;
 double busy_time(const KernelConfig& c, int occ, int M, int N, int K, int batch) {
   const int64_t wgs = tiles_for(c, M, N) * (int64_t)(batch < kMaxGridY ? batch : kMaxGridY);
   const int64_t n = (wgs + kCompute - 1) / kCompute;
+  if (n <= 0) return 0.0;
   const int64_t blocks = (int64_t)(c.kgroups > 0 ? c.kgroups : 1) * (c.bm / 32) * (c.bn / 32);
   const int64_t resident = (n < occ ? n : occ) * blocks;
   const double stretch = resident >= kSatChains ? 1.0 : (double)kSatChains / (double)resident;
