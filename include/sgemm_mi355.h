@@ -67,9 +67,11 @@ extern "C" {
 #define SGEMM_MI355_OP_T 1 /* op(X) = X^T */
 
 /*
- * Main entry point: C = A.B with the kernel configuration the built-in tile
- * table picks for (M, N, K) (tile sizes chosen by measurement, as the CUDA
- * Handbook section 17.3 and GPU Parallel Book section 9.6 prescribe).
+ * Main entry point: C = A.B with the kernel configuration the built-in
+ * selection picks for (M, N, K): measured run times of the configurations on
+ * a grid of shapes, carried to other shapes by a model of how their
+ * workgroups fill the compute units (tile sizes chosen by measurement, as the
+ * CUDA Handbook section 17.3 and GPU Parallel Book section 9.6 prescribe).
  * Quick returns: M == 0 or N == 0 does nothing and returns 0; K == 0 sets the
  * M x N block of C to +0 (the empty sum). Any 4-byte-aligned pointers and any
  * leading dimensions allowed above are accepted.
@@ -221,13 +223,21 @@ int sgemm_mi355_validate_ex(int opA, int opB, int M, int N, int K, float alpha,
                             const float *B, int ldb, long long strideB,
                             float beta, const float *C, int ldc, long long strideC, int batch);
 
-/* Configuration id the tile table picks for a problem shape (host only). */
+/*
+ * Configuration id the selection picks for a plain single product of this
+ * shape (host only), assuming 16-byte aligned operands with leading
+ * dimensions that are multiples of 4; sgemm_mi355 itself checks the actual
+ * pointers and may pick a register-staged configuration for others.
+ */
 int sgemm_mi355_select_config(int M, int N, int K);
 
 /* Configuration id sgemm_mi355_valu uses for a problem shape (host only). */
 int sgemm_mi355_select_config_valu(int M, int N, int K);
 
-/* Configuration id chosen for a general/batched problem (host only). */
+/*
+ * Configuration id chosen for a general or batched problem (host only), with
+ * the same alignment assumption as sgemm_mi355_select_config.
+ */
 int sgemm_mi355_select_config_ex(int opA, int opB, int M, int N, int K, int batch);
 
 /*

@@ -6,7 +6,7 @@ summation order, so any order within the standard bound is correct):
     ||C - C64||_F / ||C64||_F <= 1e-5, C64 the FP64-accumulated reference;
   * integer inputs in {-4..4}: exact (every partial sum is an integer below
     2^24, so every order gives the same FP32 value).
-Full-size workloads run in the configuration the tile table picks (the one
+Full-size workloads run in the configuration the library selects (the one
 the benchmark times) and are checked on one random row and one random
 column in every band of 128, plus exact row/column checksums of the whole
 result for the integer variant.
