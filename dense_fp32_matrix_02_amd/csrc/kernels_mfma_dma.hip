@@ -57,7 +57,8 @@ __device__ __forceinline__ void copy16_to_lds(const float* g, float* lds) {
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Position of chunk c of a k-contiguous line r: lines two (BK = 16) or one
-// (BK = 32) 128-byte bank spans apart get different chunk permutations.
+// (BK >= 32) 128-byte bank spans apart get different chunk permutations, so
+// eight consecutive lines reading the same logical chunk hit distinct banks.
 template <int BK>
 __device__ __forceinline__ int swz(int r) {
   return BK == 16 ? (r >> 1) & 3 : r & 7;
@@ -76,7 +77,7 @@ struct Slab {
   static constexpr int PER_WAVE = REGIONS / NW;        // direct loads per wave per slab
   static constexpr int CHUNKS = FLOATS / 4 / NT;       // register-staged chunks per thread
   static constexpr int CPL = KCONTIG ? BK / 4 : ROWS / 4;  // 16-byte chunks per LDS row
-  static_assert(!KCONTIG || BK == 16 || BK == 32, "swizzle is defined for 16- and 32-deep slabs");
+  static_assert(!KCONTIG || BK == 16 || BK % 32 == 0, "swizzle is defined for 16-deep and 32k-deep slabs");
   static_assert(ROWS % 32 == 0 && REGIONS % NW == 0, "whole 1 KiB regions per wave");
   static_assert((FLOATS / 4) % NT == 0, "whole chunks per thread");
 
@@ -171,29 +172,44 @@ struct Slab {
   }
 };
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int TA_ = 0, int TB_ = 0>
+// KG > 1 splits each slab's k range among KG groups of WM x WN waves (every
+// wave still takes part in the loads); after the last slab the groups' sums
+// are added in ascending group order through the then idle stage buffers.
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_, int TA_ = 0, int TB_ = 0, int KG_ = 1>
 struct DmaCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
-  static constexpr int TA = TA_, TB = TB_;
-  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int TA = TA_, TB = TB_, KG = KG_;
+  static constexpr int NW = WM * WN * KG, NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
+  static constexpr int KSUB = BK / KG;  // k values of each slab per group
   // op(A) = A has k-contiguous rows; op(B) = B^T has k-contiguous columns.
   using SlabA = Slab<BM, BK, TA == 0, NW>;
   using SlabB = Slab<BN, BK, TB != 0, NW>;
   static constexpr int LDS_BYTES = 4 * STAGES * (SlabA::FLOATS + SlabB::FLOATS);
+  // partial sums of groups 1..KG-1, BM*BN floats each, packed into the stage arrays
+  static constexpr int RED_PER_ARRAY =
+      (SlabA::FLOATS < SlabB::FLOATS ? SlabA::FLOATS : SlabB::FLOATS) / (BM * BN);
   static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile must be 32x32 blocks");
   static_assert(STAGES >= 2 && STAGES <= 3, "two or three LDS stages");
+  static_assert(NT <= 1024, "at most 16 waves per workgroup");
+  static_assert(KG == 1 || (KSUB % 32 == 0 && KSUB * KG == BK), "each group takes whole 32-deep k ranges");
+  static_assert(KG == 1 || KG - 1 <= RED_PER_ARRAY * 2 * STAGES, "group sums fit in the stage arrays");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
+  // Waves per SIMD the direct kernel's registers must allow: four, or as many
+  // as the workgroups that fit in LDS can bring (the unused stage arrays of a
+  // two-stage kernel take up to 2 KiB more).
+  static constexpr int LDS_WGS = (160 * 1024) / (LDS_BYTES + 2048);
+  static constexpr int WAVES_EU = LDS_WGS * NW / 4 < 4 ? (LDS_WGS * NW / 4 > 1 ? LDS_WGS * NW / 4 : 1) : 4;
 };
 
 // DIRECT: every slab by direct loads (the launcher guarantees 16-byte aligned
 // chunks inside the matrices and K a multiple of BK); otherwise every slab
 // through registers. Two kernels rather than a branch, so each gets the
-// registers it needs. The direct kernels are held to 128 VGPRs (four waves
-// per SIMD), so small tiles keep several workgroups per compute unit instead
-// of spending the register file on one.
+// registers it needs. The direct kernels are held to the registers of
+// WAVES_EU waves per SIMD (128 VGPRs for four), so small tiles keep several
+// workgroups per compute unit instead of spending the register file on one.
 template <class Cfg, bool DIRECT>
-__global__ void __launch_bounds__(Cfg::NT, DIRECT ? 4 : 1) mfma_dma_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_kernel(GemmArgs g) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int ST = Cfg::STAGES, NW = Cfg::NW;
   using SA = typename Cfg::SlabA;
@@ -229,7 +245,9 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? 4 : 1) mfma_dma_kernel(GemmA
   const int m0 = tm * BM, n0 = tn * BN;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave % Cfg::WM, wn = wave / Cfg::WM;
+  const int kg = Cfg::KG == 1 ? 0 : wave / (Cfg::WM * Cfg::WN);  // k group
+  const int wt = Cfg::KG == 1 ? wave : wave % (Cfg::WM * Cfg::WN);  // wave tile within the group
+  const int wm = wt % Cfg::WM, wn = wt / Cfg::WM;
   const int l32 = lane & 31, h = lane >> 5;
   const float* A = g.A + (int64_t)blockIdx.y * g.strideA;
   const float* B = g.B + (int64_t)blockIdx.y * g.strideB;
@@ -272,11 +290,15 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? 4 : 1) mfma_dma_kernel(GemmA
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // Group kg multiplies k = kg*KSUB .. (kg+1)*KSUB - 1 of each slab; KSUB is a
+  // multiple of 32, so for k-contiguous slabs that offset commutes with the
+  // fragment swizzle.
+  const int kbase = kg * Cfg::KSUB;
   auto compute = [&](auto stage) {
-    const float* as = SA::frag_base(stage_a(stage), wm * Cfg::WTM, l32, h);
-    const float* bs = SB::frag_base(stage_b(stage), wn * Cfg::WTN, l32, h);
+    const float* as = SA::frag_base(stage_a(stage), wm * Cfg::WTM, l32, h) + SA::k_offset(kbase, BM);
+    const float* bs = SB::frag_base(stage_b(stage), wn * Cfg::WTN, l32, h) + SB::k_offset(kbase, BN);
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 8) {
+    for (int kk = 0; kk < Cfg::KSUB; kk += 8) {
       f32x4 af[FM], bf[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) af[i] = SA::frag(as, i, kk, akey);
@@ -355,6 +377,40 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? 4 : 1) mfma_dma_kernel(GemmA
     if (s < nk) rstep(S0{}, s);
   }
 
+  // ---- k groups: add the groups' sums in ascending group order ----------
+  if constexpr (Cfg::KG > 1) {
+    constexpr int WAVE_FLOATS = FM * FN * 16 * 64;  // one wave's accumulators
+    // Partial sums of group q (1..KG-1) go to block q-1 of the stage arrays
+    // As0, Bs0, As1, Bs1, ... (RED_PER_ARRAY blocks of BM*BN floats each).
+    auto red_block = [&](int q) -> float* {
+      const int a = (q - 1) / Cfg::RED_PER_ARRAY, off = ((q - 1) % Cfg::RED_PER_ARRAY) * BM * BN;
+      float* base = a == 0 ? As0 : a == 1 ? Bs0 : a == 2 ? As1 : a == 3 ? Bs1 : a == 4 ? As2 : Bs2;
+      return base + off + wt * WAVE_FLOATS + lane;
+    };
+    // The K loop ends with a barrier, so no wave still reads a slab.
+    if (kg > 0) {
+      float* red = red_block(kg);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int q = 1; q < Cfg::KG; ++q) {
+      const float* red = red_block(q);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * FN + j) * 16 + r) * 64];
+    }
+  }
+
   // ---- epilogue: masked stores; C is read only when beta != 0 ------------
   float* C = g.C + (int64_t)blockIdx.y * g.strideC;
   const int row0 = m0 + wm * Cfg::WTM + 4 * h;
@@ -407,18 +463,25 @@ hipError_t launch_mfma_dma(const GemmArgs& g, hipStream_t stream) {
 
 }  // namespace
 
-// Name: mfma32_<BM>x<BN>x<BK>_w<WM>x<WN>_lds<STAGES>[_<ops>]: direct
-// global-to-LDS staging with STAGES LDS buffers; <ops> = tn, nt or tt names
-// transposed operands (first letter A, second B), none the plain product.
-#define SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, ST, TA, TB, SFX)                                        \
-  {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_lds" #ST SFX, KIND_MFMA, BM, BN, BK, 64 * WM * WN, \
-   TA, TB, &launch_mfma_dma<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB>>,                                  \
-   reinterpret_cast<const void*>(&mfma_dma_kernel<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB>, true>), 1}
-#define SGEMM_MFMA_DMA(BM, BN, BK, WM, WN, ST) SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, ST, 0, 0, "")
-#define SGEMM_MFMA_DMA_OPS(BM, BN, BK, WM, WN, ST)                      \
-  SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, ST, 1, 0, "_tn"),              \
-      SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, ST, 0, 1, "_nt"),          \
-      SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, ST, 1, 1, "_tt")
+// Name: mfma32_<BM>x<BN>x<BK>_w<WM>x<WN>[_kg<KG>]_lds<STAGES>[_<ops>]: direct
+// global-to-LDS staging with STAGES LDS buffers; _kg<KG> splits each slab's k
+// range among KG wave groups; <ops> = tn, nt or tt names transposed operands
+// (first letter A, second B), none the plain product.
+#define SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, KG, ST, TA, TB, SFX)                                      \
+  {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SFX, KIND_MFMA, BM, BN, BK, 64 * WM * WN * KG, TA, TB,  \
+   &launch_mfma_dma<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB, KG>>,                                         \
+   reinterpret_cast<const void*>(&mfma_dma_kernel<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB, KG>, true>), KG}
+#define SGEMM_MFMA_DMA(BM, BN, BK, WM, WN, ST) SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, 1, ST, 0, 0, "_lds" #ST)
+#define SGEMM_MFMA_DMA_OPS(BM, BN, BK, WM, WN, ST)                                  \
+  SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, 1, ST, 1, 0, "_lds" #ST "_tn"),            \
+      SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, 1, ST, 0, 1, "_lds" #ST "_nt"),        \
+      SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, 1, ST, 1, 1, "_lds" #ST "_tt")
+#define SGEMM_MFMA_DMA_KG(BM, BN, BK, WM, WN, KG, ST) \
+  SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, KG, ST, 0, 0, "_kg" #KG "_lds" #ST)
+#define SGEMM_MFMA_DMA_KG_OPS(BM, BN, BK, WM, WN, KG, ST)                                  \
+  SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, KG, ST, 1, 0, "_kg" #KG "_lds" #ST "_tn"),        \
+      SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, KG, ST, 0, 1, "_kg" #KG "_lds" #ST "_nt"),    \
+      SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, KG, ST, 1, 1, "_kg" #KG "_lds" #ST "_tt")
 
 KernelConfig kMfmaDmaConfigs[] = {
     // 256x256 block tile, 16 waves of 64x64, two stages: one workgroup per CU
@@ -432,6 +495,12 @@ KernelConfig kMfmaDmaConfigs[] = {
     SGEMM_MFMA_DMA_OPS(256, 128, 16, 4, 2, 2),
     SGEMM_MFMA_DMA(128, 256, 16, 2, 4, 2),
     SGEMM_MFMA_DMA_OPS(128, 256, 16, 2, 4, 2),
+    // k groups: more waves on the small tiles of long-K shapes
+    SGEMM_MFMA_DMA_KG(64, 64, 64, 2, 2, 2, 2),
+    SGEMM_MFMA_DMA_KG(32, 32, 128, 1, 1, 4, 2),
+    SGEMM_MFMA_DMA_KG_OPS(32, 32, 128, 1, 1, 4, 2),
+    SGEMM_MFMA_DMA_KG(32, 32, 256, 1, 1, 8, 2),
+    SGEMM_MFMA_DMA_KG_OPS(32, 32, 256, 1, 1, 8, 2),
 };
 const int kNumMfmaDmaConfigs = sizeof(kMfmaDmaConfigs) / sizeof(kMfmaDmaConfigs[0]);
 
