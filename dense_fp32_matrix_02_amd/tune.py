@@ -146,12 +146,15 @@ def main(argv=None):
                          "(powers of two) for the table's split-K block (no per-configuration timings)")
     ap.add_argument("--json", default=None)
     ap.add_argument("--table", default=None)
-    ap.add_argument("--from-json", default=None, metavar="JSON",
-                    help="write --table from a saved --json result instead of measuring")
+    ap.add_argument("--from-json", default=None, metavar="JSON[,JSON...]",
+                    help="write --table from saved --json results (one file per op pair, plus the "
+                         "split-K grid) instead of measuring")
     ap.add_argument("--ops", default="nn", choices=["nn", "tn", "nt", "tt"])
     ap.add_argument("--batch", type=int, default=1)
     args = ap.parse_args(argv)
     opA, opB = int(args.ops[0] == "t"), int(args.ops[1] == "t")
+    if args.from_json and not args.table:
+        ap.error("--from-json writes a table: give --table")
     if args.table and args.batch != 1:
         ap.error("--table records single products: leave --batch at 1")
     if args.splitk and (opA or opB or args.batch != 1):
@@ -207,7 +210,7 @@ def main(argv=None):
         if mfma:
             row["best"] = min(mfma, key=mfma.get)
             row["default"] = names[sg.sgemm_mi355_select_config_ex(opA, opB, M, N, K, args.batch)]
-            print(f"  best {row['best']}  (table/rule picks {row['default']})", flush=True)
+            print(f"  best {row['best']}  (selection picks {row['default']})", flush=True)
         results.append(row)
         del Ad, Bd, C
     if args.json:
