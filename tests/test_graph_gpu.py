@@ -118,3 +118,32 @@ def test_graph_strided_batch():
     nan = torch.full((batch, M, N), float("nan"), device="cuda")
     want = np.stack([oracle.sgemm_f32(A[b], B[b]) for b in range(batch)])
     _replay_and_check(graph, C, nan, want, "batched")
+
+
+def test_graph_direct_lds_kernels():
+    """Direct global-to-LDS kernels under capture: a batch the selection runs
+    in the 256x256 direct tile, and a transposed product it runs in the 32x32
+    direct tile whose k groups add their sums through LDS."""
+    batch, M, N, K = 16, 1024, 1024, 1024
+    A = np.stack([_ints(M, K, 50 + b) for b in range(batch)])
+    B = np.stack([_ints(K, N, 70 + b) for b in range(batch)])
+    print(f"[gpu] graph batched selects {sg.config_names()[sg.sgemm_mi355_select_config_ex(0, 0, M, N, K, batch)]}",
+          flush=True)
+    Ad, Bd = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    C = torch.empty((batch, M, N), device="cuda")
+    graph = _capture(lambda: sg.gemm_strided_batched(Ad, Bd, C))
+    want = np.matmul(A.astype(np.float64), B.astype(np.float64)).astype(np.float32)
+    np.testing.assert_array_equal(want[3], oracle.sgemm_f32(A[3], B[3]))
+    nan = torch.full((batch, M, N), float("nan"), device="cuda")
+    _replay_and_check(graph, C, nan, want, "direct 256x256 batch")
+
+    M, N, K = 512, 512, 4096
+    At, Bt = _ints(K, M, 91), _ints(N, K, 92)  # stored transposed: op(A) = At^T, op(B) = Bt^T
+    print(f"[gpu] graph tt selects {sg.config_names()[sg.sgemm_mi355_select_config_ex(1, 1, M, N, K, 1)]}",
+          flush=True)
+    Ad, Bd = torch.from_numpy(At).cuda(), torch.from_numpy(Bt).cuda()
+    C = torch.empty((M, N), device="cuda")
+    graph = _capture(lambda: sg.gemm(Ad, Bd, C, opA=1, opB=1))
+    want = oracle.sgemm_f32(np.ascontiguousarray(At.T), np.ascontiguousarray(Bt.T))
+    nan = torch.full((M, N), float("nan"), device="cuda")
+    _replay_and_check(graph, C, nan, want, "direct k-group tt")
