@@ -59,6 +59,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sgemm_mi355_splitk_workspace_size.argtypes = [_I, _I, _I, _I]
     lib.sgemm_mi355_splitk_workspace_size.restype = ctypes.c_size_t
     lib.sgemm_mi355_select_splitk.argtypes = [_I, _I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]
+    lib.sgemm_mi355_streamk.argtypes = _GEMM_EX[:-1] + [_P, ctypes.c_size_t, _P]
+    lib.sgemm_mi355_streamk_with_config.argtypes = _GEMM_EX[:-1] + [_P, ctypes.c_size_t, _P, _I]
+    lib.sgemm_mi355_streamk_workspace_size.argtypes = [_I] * 6
+    lib.sgemm_mi355_streamk_workspace_size.restype = ctypes.c_size_t
+    lib.sgemm_mi355_select_streamk.argtypes = [_I, _I, _I, _I, _I, ctypes.POINTER(_I)]
+    lib.sgemm_mi355_config_streamk.argtypes = [_I]
     lib.sgemm_mi355_validate.argtypes = [_I, _I, _I, _P, _I, _P, _I, _P, _I]
     lib.sgemm_mi355_validate_ex.argtypes = [_I, _I, _I, _I, _I, _F, _P, _I, _LL, _P, _I, _LL, _F, _P,
                                             _I, _LL, _I]
@@ -82,7 +88,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                  "sgemm_mi355_strided_batched_with_config", "sgemm_mi355_validate_ex",
                  "sgemm_mi355_select_config_ex", "sgemm_mi355_config_ops", "sgemm_mi355_splitk",
                  "sgemm_mi355_splitk_with_config", "sgemm_mi355_select_splitk",
-                 "sgemm_mi355_select_config_valu"):
+                 "sgemm_mi355_select_config_valu", "sgemm_mi355_streamk", "sgemm_mi355_streamk_with_config",
+                 "sgemm_mi355_select_streamk", "sgemm_mi355_config_streamk"):
         getattr(lib, name).restype = _I
     _lib = lib
     return lib
@@ -143,6 +150,35 @@ def sgemm_mi355_select_splitk(opA, opB, M, N, K):
     if rc != OK:
         raise SgemmError(rc, "sgemm_mi355_select_splitk")
     return sp.value, cf.value
+
+
+def sgemm_mi355_streamk(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes,
+                        stream) -> int:
+    return load().sgemm_mi355_streamk(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                                      workspace_bytes, stream)
+
+
+def sgemm_mi355_streamk_with_config(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                                    workspace_bytes, stream, config) -> int:
+    return load().sgemm_mi355_streamk_with_config(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                                  workspace, workspace_bytes, stream, config)
+
+
+def sgemm_mi355_streamk_workspace_size(opA, opB, M, N, K, config=-1) -> int:
+    return load().sgemm_mi355_streamk_workspace_size(opA, opB, M, N, K, config)
+
+
+def sgemm_mi355_select_streamk(opA, opB, M, N, K) -> int:
+    """The configuration the stream-K call would run, or -1 (plain path); raises on bad arguments."""
+    cf = _I()
+    rc = load().sgemm_mi355_select_streamk(opA, opB, M, N, K, ctypes.byref(cf))
+    if rc != OK:
+        raise SgemmError(rc, "sgemm_mi355_select_streamk")
+    return cf.value
+
+
+def sgemm_mi355_config_streamk(config) -> int:
+    return load().sgemm_mi355_config_streamk(config)
 
 
 def sgemm_mi355_validate_ex(opA, opB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB, beta, C, ldc,
@@ -389,4 +425,35 @@ def gemm_splitk(A, B, C=None, *, splits: int | None = None, opA: int = OP_N, opB
     rc = (sgemm_mi355_splitk(*args) if config is None else sgemm_mi355_splitk_with_config(*args, config))
     if rc != OK:
         raise SgemmError(rc, "sgemm_mi355_splitk")
+    return C
+
+
+def gemm_streamk(A, B, C=None, *, opA: int = OP_N, opB: int = OP_N, alpha: float = 1.0, beta: float = 0.0,
+                 workspace=None, config: int | None = None, stream=None):
+    """Stream-K product C = alpha*op(A).op(B) + beta*C through the C ABI.
+
+    Without ``config`` the library chooses (and may run the plain path); the
+    workspace (a float32 GPU tensor of at least
+    sgemm_mi355_streamk_workspace_size bytes, 16-byte aligned) is allocated
+    with torch when omitted. Returns C.
+    """
+    import torch
+
+    M, K = _op_dims(A, opA)
+    K2, N = _op_dims(B, opB)
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs an input C")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    need = sgemm_mi355_streamk_workspace_size(opA, opB, M, N, K, -1 if config is None else config)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=A.device)
+    s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
+    args = (opA, opB, M, N, K, alpha, A.data_ptr(), _ld(A, "A"), B.data_ptr(), _ld(B, "B"), beta,
+            C.data_ptr(), _ld(C, "C"), workspace.data_ptr(), workspace.numel() * 4, s)
+    rc = (sgemm_mi355_streamk(*args) if config is None else sgemm_mi355_streamk_with_config(*args, config))
+    if rc != OK:
+        raise SgemmError(rc, "sgemm_mi355_streamk")
     return C

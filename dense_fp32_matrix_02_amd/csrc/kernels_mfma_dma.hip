@@ -202,55 +202,57 @@ struct DmaCfg {
   static constexpr int WAVES_EU = LDS_WGS * NW / 4 < 4 ? (LDS_WGS * NW / 4 > 1 ? LDS_WGS * NW / 4 : 1) : 4;
 };
 
+// The LDS stage arrays of a kernel. Each stage is its own __shared__ array,
+// and code picks one with a compile-time index: the compiler then sees that a
+// direct load into one stage does not alias reads of another, and does not
+// make those reads wait for the load.
+struct Stages {
+  float* a[3];
+  float* b[3];
+};
+
+#define SGEMM_DMA_DECLARE_STAGES(Cfg, st)                                                     \
+  __shared__ __attribute__((aligned(1024))) float As0[Cfg::SlabA::FLOATS];                    \
+  __shared__ __attribute__((aligned(1024))) float As1[Cfg::SlabA::FLOATS];                    \
+  __shared__ __attribute__((aligned(1024))) float As2[Cfg::STAGES > 2 ? Cfg::SlabA::FLOATS : 4]; \
+  __shared__ __attribute__((aligned(1024))) float Bs0[Cfg::SlabB::FLOATS];                    \
+  __shared__ __attribute__((aligned(1024))) float Bs1[Cfg::SlabB::FLOATS];                    \
+  __shared__ __attribute__((aligned(1024))) float Bs2[Cfg::STAGES > 2 ? Cfg::SlabB::FLOATS : 4]; \
+  const Stages st{{As0, As1, As2}, {Bs0, Bs1, Bs2}}
+
 // DIRECT: every slab by direct loads (the launcher guarantees 16-byte aligned
 // chunks inside the matrices and K a multiple of BK); otherwise every slab
 // through registers. Two kernels rather than a branch, so each gets the
 // registers it needs. The direct kernels are held to the registers of
 // WAVES_EU waves per SIMD (128 VGPRs for four), so small tiles keep several
 // workgroups per compute unit instead of spending the register file on one.
-template <class Cfg, bool DIRECT>
-__global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_kernel(GemmArgs g) {
-  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
+//
+// tile_product: the workgroup's BM x BN tile of op(A).op(B) at rows m0.., columns
+// n0.., over k = 0 .. K-1 of the operands whose k = 0 lies at A and B. It hands
+// the accumulators to epi(acc, row0, col0) (with k groups, group 0 only, after the
+// groups' sums are added), where accumulator element r of block (i, j) belongs to
+// row row0 + 32 i + 8 (r / 4) + r % 4 and column col0 + 32 j. Every slab step
+// ends with a barrier, so when it returns no wave still reads the stage arrays.
+template <class Cfg, bool DIRECT, class Epi>
+__device__ __forceinline__ void tile_product(const GemmArgs& g, const Stages& st, const float* A, const float* B,
+                                             int K, int m0, int n0, Epi&& epi) {
+  constexpr int BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int ST = Cfg::STAGES, NW = Cfg::NW;
   using SA = typename Cfg::SlabA;
   using SB = typename Cfg::SlabB;
-  // One array per stage, selected at compile time: the compiler can then see
-  // that a direct load into one stage does not alias reads of another, and
-  // does not make those reads wait for the load.
-  __shared__ __attribute__((aligned(1024))) float As0[SA::FLOATS];
-  __shared__ __attribute__((aligned(1024))) float As1[SA::FLOATS];
-  __shared__ __attribute__((aligned(1024))) float As2[ST > 2 ? SA::FLOATS : 4];
-  __shared__ __attribute__((aligned(1024))) float Bs0[SB::FLOATS];
-  __shared__ __attribute__((aligned(1024))) float Bs1[SB::FLOATS];
-  __shared__ __attribute__((aligned(1024))) float Bs2[ST > 2 ? SB::FLOATS : 4];
-  auto stage_a = [&](auto st) -> float* {
-    if constexpr (decltype(st)::value == 0) return As0;
-    else if constexpr (decltype(st)::value == 1) return As1;
-    else return As2;
-  };
-  auto stage_b = [&](auto st) -> float* {
-    if constexpr (decltype(st)::value == 0) return Bs0;
-    else if constexpr (decltype(st)::value == 1) return Bs1;
-    else return Bs2;
-  };
+  auto stage_a = [&](auto s) -> float* { return st.a[decltype(s)::value]; };
+  auto stage_b = [&](auto s) -> float* { return st.b[decltype(s)::value]; };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
 
   const int M = g.M, N = g.N;
-  const int K = (blockIdx.y == gridDim.y - 1) ? g.k_last : g.K;  // last split-K chunk may be short
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int kg = Cfg::KG == 1 ? 0 : wave / (Cfg::WM * Cfg::WN);  // k group
   const int wt = Cfg::KG == 1 ? wave : wave % (Cfg::WM * Cfg::WN);  // wave tile within the group
   const int wm = wt % Cfg::WM, wn = wt / Cfg::WM;
   const int l32 = lane & 31, h = lane >> 5;
-  const float* A = g.A + (int64_t)blockIdx.y * g.strideA;
-  const float* B = g.B + (int64_t)blockIdx.y * g.strideB;
 
   // ---- direct loads: region q = p*NW + wave of each slab is this wave's ----
   const float* a_src[SA::PER_WAVE];
@@ -295,8 +297,8 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
   // fragment swizzle.
   const int kbase = kg * Cfg::KSUB;
   auto compute = [&](auto stage) {
-    const float* as = SA::frag_base(stage_a(stage), wm * Cfg::WTM, l32, h) + SA::k_offset(kbase, BM);
-    const float* bs = SB::frag_base(stage_b(stage), wn * Cfg::WTN, l32, h) + SB::k_offset(kbase, BN);
+    const float* as = SA::frag_base(stage_a(stage), wm * Cfg::WTM, l32, h) + SA::k_offset(kbase, Cfg::BM);
+    const float* bs = SB::frag_base(stage_b(stage), wn * Cfg::WTN, l32, h) + SB::k_offset(kbase, Cfg::BN);
 #pragma unroll
     for (int kk = 0; kk < Cfg::KSUB; kk += 8) {
       f32x4 af[FM], bf[FN];
@@ -381,10 +383,15 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
   if constexpr (Cfg::KG > 1) {
     constexpr int WAVE_FLOATS = FM * FN * 16 * 64;  // one wave's accumulators
     // Partial sums of group q (1..KG-1) go to block q-1 of the stage arrays
-    // As0, Bs0, As1, Bs1, ... (RED_PER_ARRAY blocks of BM*BN floats each).
+    // a0, b0, a1, b1, ... (RED_PER_ARRAY blocks of BM*BN floats each).
     auto red_block = [&](int q) -> float* {
-      const int a = (q - 1) / Cfg::RED_PER_ARRAY, off = ((q - 1) % Cfg::RED_PER_ARRAY) * BM * BN;
-      float* base = a == 0 ? As0 : a == 1 ? Bs0 : a == 2 ? As1 : a == 3 ? Bs1 : a == 4 ? As2 : Bs2;
+      const int a = (q - 1) / Cfg::RED_PER_ARRAY, off = ((q - 1) % Cfg::RED_PER_ARRAY) * Cfg::BM * Cfg::BN;
+      float* base = a == 0   ? st.a[0]
+                    : a == 1 ? st.b[0]
+                    : a == 2 ? st.a[1]
+                    : a == 3 ? st.b[1]
+                    : a == 4 ? st.a[2]
+                             : st.b[2];
       return base + off + wt * WAVE_FLOATS + lane;
     };
     // The K loop ends with a barrier, so no wave still reads a slab.
@@ -410,12 +417,15 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
           for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * FN + j) * 16 + r) * 64];
     }
   }
+  epi(acc, m0 + wm * Cfg::WTM + 4 * h, n0 + wn * Cfg::WTN + l32);
+}
 
-  // ---- epilogue: masked stores; C is read only when beta != 0 ------------
-  float* C = g.C + (int64_t)blockIdx.y * g.strideC;
-  const int row0 = m0 + wm * Cfg::WTM + 4 * h;
-  const int col0 = n0 + wn * Cfg::WTN + l32;
-  const float alpha = g.alpha, beta = g.beta;
+// C = alpha * acc + beta * C over the accumulators of one wave (rows and
+// columns as tile_product hands them over), masked to the M x N matrix; C is
+// read only when beta != 0.
+template <int FM, int FN>
+__device__ __forceinline__ void store_c(const f32x16 (&acc)[FM][FN], int row0, int col0, float* C, int64_t ldc,
+                                        int M, int N, float alpha, float beta) {
   auto store_tile = [&](auto op) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -425,7 +435,7 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = row0 + 32 * i + 8 * (r >> 2) + (r & 3);
-          if (row < M && col < N) op(C + (int64_t)row * g.ldc + col, acc[i][j][r]);
+          if (row < M && col < N) op(C + (int64_t)row * ldc + col, acc[i][j][r]);
         }
       }
   };
@@ -435,6 +445,129 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
     store_tile([alpha](float* p, float v) { *p = alpha * v; });
   else
     store_tile([alpha, beta](float* p, float v) { *p = __builtin_fmaf(beta, *p, alpha * v); });
+}
+
+// One workgroup per tile of C (grid.x) and batch entry (grid.y).
+template <class Cfg, bool DIRECT>
+__global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_kernel(GemmArgs g) {
+  SGEMM_DMA_DECLARE_STAGES(Cfg, st);
+  const int K = (blockIdx.y == gridDim.y - 1) ? g.k_last : g.K;  // last split-K chunk may be short
+  const int tiles_m = (g.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (g.N + Cfg::BN - 1) / Cfg::BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
+  const float* A = g.A + (int64_t)blockIdx.y * g.strideA;
+  const float* B = g.B + (int64_t)blockIdx.y * g.strideB;
+  float* C = g.C + (int64_t)blockIdx.y * g.strideC;
+  tile_product<Cfg, DIRECT>(g, st, A, B, K, tm * Cfg::BM, tn * Cfg::BN,
+                            [&](const f32x16(&acc)[Cfg::FM][Cfg::FN], int row0, int col0) {
+                              store_c(acc, row0, col0, C, g.ldc, g.M, g.N, g.alpha, g.beta);
+                            });
+}
+
+// Stream-K (Osama et al., "Stream-K: Work-centric Parallel Decomposition for
+// Dense Matrix-Matrix Multiplication on the GPU", PPoPP 2023): a persistent
+// grid of G workgroups, about one per resident slot of the device. The first
+// dp_tiles tiles of the tile order run whole, tile j on workgroup j % G. The
+// remaining sk_tiles tiles are cut into their iters BK-deep slabs, and the
+// sk_tiles * iters slabs (in tile order, k ascending within a tile) are dealt
+// out as G contiguous ranges: workgroup w takes slabs [w U / G, (w+1) U / G),
+// U = sk_tiles * iters. A range crosses tile boundaries; each piece of a tile
+// it holds is a segment. A segment that spans its whole tile is stored to C;
+// any other is a partial sum, stored as a dense row-major BM x BN block in
+// slot 2w (the range's first segment) or 2w+1 (its last) of the workspace
+// (StreamKPlan). A second kernel then adds each split tile's partials in
+// ascending k order. Every workgroup's loop ends after its own range, so the
+// grid drains whether or not all of it is resident at once.
+template <class Cfg, bool DIRECT>
+__global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1)
+    mfma_dma_streamk_kernel(GemmArgs g, StreamKPlan p) {
+  static_assert(Cfg::KG == 1, "stream-K runs tiles without k groups");
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+  SGEMM_DMA_DECLARE_STAGES(Cfg, st);
+  using SA = typename Cfg::SlabA;
+  using SB = typename Cfg::SlabB;
+  const int G = gridDim.x, w = blockIdx.x;
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int n_dp = w < p.dp_tiles ? (p.dp_tiles - 1 - w) / G + 1 : 0;
+  const int64_t begin = (int64_t)w * p.sk_iters / G, end = (int64_t)(w + 1) * p.sk_iters / G;
+  int64_t it = begin;
+  for (int item = 0;; ++item) {
+    int tile, kb, ke;
+    if (item < n_dp) {
+      tile = w + item * G;
+      kb = 0;
+      ke = p.iters;
+    } else {
+      if (it >= end) break;
+      const int u = (int)(it / p.iters);
+      kb = (int)(it - (int64_t)u * p.iters);
+      ke = (end - it) < (int64_t)(p.iters - kb) ? kb + (int)(end - it) : p.iters;
+      tile = p.dp_tiles + u;
+    }
+    const bool whole = kb == 0 && ke == p.iters;
+    float* slot = p.partials + (size_t)(2 * w + (it == begin ? 0 : 1)) * (BM * BN);
+    if (item >= n_dp) it += ke - kb;
+    int tm, tn;
+    tile_coords(tile, tiles_m, tiles_n, 4, tm, tn);
+    const int k0 = kb * BK;
+    const int klen = ((int64_t)ke * BK < (int64_t)g.K ? ke * BK : g.K) - k0;
+    const int m0 = tm * BM, n0 = tn * BN;
+    tile_product<Cfg, DIRECT>(
+        g, st, g.A + SA::k_offset(k0, g.lda), g.B + SB::k_offset(k0, g.ldb), klen, m0, n0,
+        [&](const f32x16(&acc)[Cfg::FM][Cfg::FN], int row0, int col0) {
+          if (whole) {
+            store_c(acc, row0, col0, g.C, g.ldc, g.M, g.N, g.alpha, g.beta);
+          } else {
+            // the whole block, edges included (the fixup masks them)
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+              for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                  slot[(row0 - m0 + 32 * i + 8 * (r >> 2) + (r & 3)) * BN + col0 - n0 + 32 * j] = acc[i][j][r];
+          }
+        });
+  }
+}
+
+// Adds the partial sums of the stream-K tiles that were split: tile
+// dp_tiles + blockIdx.y, 1024 consecutive elements of its row-major BM x BN
+// block per workgroup (4 columns per thread). The workgroups holding pieces of
+// the tile are those whose slab ranges meet [u iters, (u+1) iters); their
+// blocks are added in ascending workgroup order, which is ascending k, so
+// repeated calls give identical bits. C = alpha * sum + beta * C, masked to
+// the M x N matrix; C is read only when beta != 0.
+__global__ void __launch_bounds__(256) streamk_fixup_kernel(GemmArgs g, StreamKPlan p, int bm, int bn, int grid) {
+  const int u = blockIdx.y;
+  const int64_t it0 = (int64_t)u * p.iters, it1 = it0 + p.iters - 1;
+  const int64_t U = p.sk_iters;
+  // the workgroup whose range holds slab `it`: the last w with w U / G <= it
+  auto owner = [&](int64_t it) { return (int)(((it + 1) * grid - 1) / U); };
+  const int wa = owner(it0), wb = owner(it1);
+  if (wa == wb) return;  // the whole tile lay in one range and went straight to C
+  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= bm * bn) return;
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int w = wa; w <= wb; ++w) {
+    const int64_t b = (int64_t)w * U / grid, en = (int64_t)(w + 1) * U / grid;
+    if (b == en) continue;  // a workgroup with no slabs
+    const int block = 2 * w + (b >= it0 ? 0 : 1);
+    s += *reinterpret_cast<const f32x4*>(p.partials + (size_t)block * bm * bn + e);
+  }
+  const int tiles_m = (g.M + bm - 1) / bm, tiles_n = (g.N + bn - 1) / bn;
+  int tm, tn;
+  tile_coords(p.dp_tiles + u, tiles_m, tiles_n, 4, tm, tn);
+  const int row = tm * bm + e / bn, col = tn * bn + e % bn;
+  if (row >= g.M) return;
+  float* c = g.C + (int64_t)row * g.ldc + col;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (col + q < g.N) {
+      const float v = g.alpha * s[q];
+      c[q] = (g.beta != 0.0f) ? __builtin_fmaf(g.beta, c[q], v) : v;
+    }
+  }
 }
 
 // Direct loads need every 16-byte chunk they fetch to be aligned and inside
@@ -461,6 +594,26 @@ hipError_t launch_mfma_dma(const GemmArgs& g, hipStream_t stream) {
   return hipLaunchKernel(kernel, dim3((unsigned)tiles, (unsigned)g.batch), dim3(Cfg::NT), args, 0, stream);
 }
 
+template <class Cfg>
+hipError_t launch_mfma_dma_streamk(const GemmArgs& g, const StreamKPlan& plan, int grid, bool direct,
+                                   hipStream_t stream) {
+  // the direct kernel only where its loads stay aligned and inside the matrices
+  if (direct && !direct_ok<Cfg>(g)) return hipErrorInvalidValue;
+  if (grid <= 0 || plan.iters <= 0 || (plan.sk_tiles > 0 && plan.partials == nullptr)) return hipErrorInvalidValue;
+  GemmArgs a = g;
+  StreamKPlan pl = plan;
+  void* args[] = {&a, &pl};
+  const void* kernel = direct ? reinterpret_cast<const void*>(&mfma_dma_streamk_kernel<Cfg, true>)
+                              : reinterpret_cast<const void*>(&mfma_dma_streamk_kernel<Cfg, false>);
+  hipError_t err = hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(Cfg::NT), args, 0, stream);
+  if (err != hipSuccess || plan.sk_tiles == 0) return err;
+  int bm = Cfg::BM, bn = Cfg::BN, gr = grid;
+  void* fargs[] = {&a, &pl, &bm, &bn, &gr};
+  const unsigned parts = (unsigned)((Cfg::BM * Cfg::BN + 1023) / 1024);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&streamk_fixup_kernel), dim3(parts, (unsigned)plan.sk_tiles),
+                         dim3(256), fargs, 0, stream);
+}
+
 }  // namespace
 
 // Name: mfma32_<BM>x<BN>x<BK>_w<WM>x<WN>[_kg<KG>]_lds<STAGES>[_<ops>]: direct
@@ -470,12 +623,21 @@ hipError_t launch_mfma_dma(const GemmArgs& g, hipStream_t stream) {
 #define SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, KG, ST, TA, TB, SFX)                                      \
   {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SFX, KIND_MFMA, BM, BN, BK, 64 * WM * WN * KG, TA, TB,  \
    &launch_mfma_dma<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB, KG>>,                                         \
-   reinterpret_cast<const void*>(&mfma_dma_kernel<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB, KG>, true>), KG}
-#define SGEMM_MFMA_DMA(BM, BN, BK, WM, WN, ST) SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, 1, ST, 0, 0, "_lds" #ST)
+   reinterpret_cast<const void*>(&mfma_dma_kernel<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB, KG>, true>), KG, \
+   nullptr, {nullptr, nullptr}}
+// The same with a stream-K form (configurations without k groups).
+#define SGEMM_MFMA_DMA_SK_CFG(BM, BN, BK, WM, WN, ST, TA, TB, SFX)                                         \
+  {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SFX, KIND_MFMA, BM, BN, BK, 64 * WM * WN, TA, TB,        \
+   &launch_mfma_dma<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB, 1>>,                                           \
+   reinterpret_cast<const void*>(&mfma_dma_kernel<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB, 1>, true>), 1,    \
+   &launch_mfma_dma_streamk<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB, 1>>,                                   \
+   {reinterpret_cast<const void*>(&mfma_dma_streamk_kernel<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB, 1>, false>), \
+    reinterpret_cast<const void*>(&mfma_dma_streamk_kernel<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB, 1>, true>)}}
+#define SGEMM_MFMA_DMA(BM, BN, BK, WM, WN, ST) SGEMM_MFMA_DMA_SK_CFG(BM, BN, BK, WM, WN, ST, 0, 0, "_lds" #ST)
 #define SGEMM_MFMA_DMA_OPS(BM, BN, BK, WM, WN, ST)                                  \
-  SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, 1, ST, 1, 0, "_lds" #ST "_tn"),            \
-      SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, 1, ST, 0, 1, "_lds" #ST "_nt"),        \
-      SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, 1, ST, 1, 1, "_lds" #ST "_tt")
+  SGEMM_MFMA_DMA_SK_CFG(BM, BN, BK, WM, WN, ST, 1, 0, "_lds" #ST "_tn"),            \
+      SGEMM_MFMA_DMA_SK_CFG(BM, BN, BK, WM, WN, ST, 0, 1, "_lds" #ST "_nt"),        \
+      SGEMM_MFMA_DMA_SK_CFG(BM, BN, BK, WM, WN, ST, 1, 1, "_lds" #ST "_tt")
 #define SGEMM_MFMA_DMA_KG(BM, BN, BK, WM, WN, KG, ST) \
   SGEMM_MFMA_DMA_CFG(BM, BN, BK, WM, WN, KG, ST, 0, 0, "_kg" #KG "_lds" #ST)
 #define SGEMM_MFMA_DMA_KG_OPS(BM, BN, BK, WM, WN, KG, ST)                                  \

@@ -40,6 +40,10 @@ struct TableBlock {
   const float* times_us;  // nshapes x ncand, row-major
   int nnorm;
   const TableNorm* norms;  // every configuration of the op pair
+  // stream-K forms: microseconds per slab of the evenly dealt work (beyond
+  // kStreamKOverheadUs), median over the stream-K grid
+  int nstreamk;
+  const TableNorm* streamk;
 };
 struct SplitShape {
   int M, N, K;
@@ -155,6 +159,9 @@ struct ResolvedBlock {
   // every configuration of the op pair: id, occupancy, median time per busy unit
   std::vector<int> gid, gocc;
   std::vector<double> gnorm;
+  // stream-K forms: id, occupancy, microseconds per slab
+  std::vector<int> skid, skocc;
+  std::vector<double> sknorm;
 };
 
 struct Resolved {
@@ -221,6 +228,16 @@ const Resolved& resolved() {
         rb.gocc.push_back(tb.norms[c].occupancy > 0 ? tb.norms[c].occupancy : 1);
         rb.gnorm.push_back(tb.norms[c].us_per_busy);
       }
+      for (int c = 0; c < tb.nstreamk && tb.streamk; ++c) {
+        const int id = config_id(tb.streamk[c].name);
+        const KernelConfig* cfg = config_at(id);
+        if (!cfg || cfg->transA != tb.opA || cfg->transB != tb.opB || cfg->streamk == nullptr ||
+            !(tb.streamk[c].us_per_busy > 0.0f))
+          continue;
+        rb.skid.push_back(id);
+        rb.skocc.push_back(tb.streamk[c].occupancy > 0 ? tb.streamk[c].occupancy : 1);
+        rb.sknorm.push_back(tb.streamk[c].us_per_busy);
+      }
       rb.norm.assign((size_t)tb.nshapes * tb.ncand, 0.0);
       for (int s = 0; s < tb.nshapes; ++s) {
         const TableShape& e = tb.shapes[s];
@@ -268,7 +285,7 @@ bool direct_path(const KernelConfig& c, int M, int N, int K, bool aligned) {
 // least predicted time, each candidate's measured time there scaled by the
 // ratio of busy_time at (M, N, K) to busy_time at the measured shape (the
 // first on a tie). -1 when no measured shape qualifies.
-int model_select(int opA, int opB, int M, int N, int K, bool aligned) {
+int model_select(int opA, int opB, int M, int N, int K, bool aligned, double* predicted_us = nullptr) {
   if (M <= 0 || N <= 0 || K <= 0) return -1;
   const ResolvedBlock& rb = resolved().block[opA][opB];
   if (!rb.src) return -1;
@@ -289,6 +306,7 @@ int model_select(int opA, int opB, int M, int N, int K, bool aligned) {
       best_t = t;
     }
   }
+  if (predicted_us) *predicted_us = best_t;
   return best;
 }
 
@@ -301,7 +319,8 @@ int model_select(int opA, int opB, int M, int N, int K, bool aligned) {
 // op pair. Over 26 measured batches (2 x 2048^3 to 4096 x 16x16x64) it
 // picks a configuration within 0.945 of the best (geometric mean), against
 // 0.836 for the rule.
-int global_select(int opA, int opB, int M, int N, int K, int batch, bool aligned) {
+int global_select(int opA, int opB, int M, int N, int K, int batch, bool aligned,
+                  double* predicted_us = nullptr) {
   if (M <= 0 || N <= 0 || K <= 0 || batch <= 0) return -1;
   const ResolvedBlock& rb = resolved().block[opA][opB];
   int best = -1;
@@ -316,6 +335,7 @@ int global_select(int opA, int opB, int M, int N, int K, int batch, bool aligned
       best_t = t;
     }
   }
+  if (predicted_us) *predicted_us = best_t;
   return best;
 }
 
@@ -542,6 +562,154 @@ void select_splitk(int opA, int opB, int M, int N, int K, int* splits, int* conf
   *config = sp.splits == 1 ? single : rule_select(opA, opB, M, N, sp.kchunk, sp.splits);
 }
 
+// ---- stream-K -----------------------------------------------------------------
+// A persistent grid of (compute units x the stream-K kernel's occupancy)
+// workgroups. The tiles of the whole rounds run whole; the slabs of the
+// tiles of the last, partial round are dealt evenly to the grid, and a
+// second kernel adds the partial sums of every tile split between
+// workgroups (StreamKPlan in sgemm_internal.h). The workspace holds two
+// BM x BN blocks per workgroup.
+
+// Compute units of the current device (0 if the runtime cannot say).
+int device_compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+
+// Workgroups of c's stream-K kernel (direct loads or register staging) one
+// compute unit holds at once (0 if the runtime cannot say).
+int streamk_occupancy(const KernelConfig& c, bool direct) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, c.streamk_kernel[direct ? 1 : 0], c.threads, 0) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+
+StreamKPlan streamk_plan(const KernelConfig& c, int M, int N, int K, int grid) {
+  const int64_t tiles = tiles_for(c, M, N);
+  const int64_t dp = tiles / grid * grid;
+  const int iters = (int)(((int64_t)K + c.bk - 1) / c.bk);
+  return StreamKPlan{(int)dp, (int)(tiles - dp), iters, (tiles - dp) * iters, nullptr};
+}
+
+uint64_t streamk_bytes(const KernelConfig& c, int grid) { return 8ull * (uint64_t)grid * c.bm * c.bn; }
+
+// Workspace c's stream-K form needs for an M x N x K product: the larger of
+// its two kernels' needs, since alignment decides which one runs.
+uint64_t streamk_need(const KernelConfig& c, int M, int N, int K) {
+  const int cus = device_compute_units();
+  uint64_t need = 0;
+  for (int d = 0; d < 2 && cus > 0 && M > 0 && N > 0 && K > 0; ++d) {
+    const int occ = streamk_occupancy(c, d != 0);
+    if (occ <= 0) continue;
+    const int grid = cus * occ;
+    if (streamk_plan(c, M, N, K, grid).sk_tiles > 0 && streamk_bytes(c, grid) > need) need = streamk_bytes(c, grid);
+  }
+  return need;
+}
+
+bool operands_aligned(const Problem& p) {
+  return ((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 15) == 0 &&
+         ((p.lda | p.ldb) & 3) == 0 && (p.batch <= 1 || ((p.strideA | p.strideB) & 3) == 0);
+}
+
+// Whether a caller workspace of `need` bytes at W overlaps A, B or C of a
+// single product.
+bool workspace_overlaps(const Problem& p, const float* C, const float* W, uint64_t need) {
+  const unsigned __int128 a_bytes =
+      4 * ((unsigned __int128)((p.opA ? p.K : p.M) - 1) * (unsigned)p.lda + (unsigned)(p.opA ? p.M : p.K));
+  const unsigned __int128 b_bytes =
+      4 * ((unsigned __int128)((p.opB ? p.N : p.K) - 1) * (unsigned)p.ldb + (unsigned)(p.opB ? p.K : p.N));
+  const unsigned __int128 c_bytes = 4 * ((unsigned __int128)(p.M - 1) * (unsigned)p.ldc + (unsigned)p.N);
+  return overlaps(W, need, p.A, a_bytes) || overlaps(W, need, p.B, b_bytes) || overlaps(W, need, C, c_bytes);
+}
+
+int run_streamk(const Problem& p, float* C, float* W, size_t w_bytes, hipStream_t stream, int config) {
+  const int v = validate(p);
+  if (v != SGEMM_MI355_OK) return v;
+  const KernelConfig* cfg = config_at(config);
+  if (cfg == nullptr || cfg->transA != p.opA || cfg->transB != p.opB || cfg->streamk == nullptr)
+    return SGEMM_MI355_ERR_CONFIG;
+  if (p.M == 0 || p.N == 0) return SGEMM_MI355_OK;
+  if (p.K == 0 || p.alpha == 0.0f) return run(p, C, stream, config);  // C = beta * C
+  const bool direct = direct_path(*cfg, p.M, p.N, p.K, operands_aligned(p));
+  const int cus = device_compute_units(), occ = streamk_occupancy(*cfg, direct);
+  if (cus <= 0 || occ <= 0) return SGEMM_MI355_ERR_LAUNCH;
+  if (tiles_for(*cfg, p.M, p.N) > INT_MAX / 2) return SGEMM_MI355_ERR_EXTENT;
+  const int grid = cus * occ;
+  StreamKPlan plan = streamk_plan(*cfg, p.M, p.N, p.K, grid);
+  if (plan.sk_tiles == 0) return run(p, C, stream, config);  // whole rounds only: the plain launch
+  const uint64_t need = streamk_bytes(*cfg, grid);
+  if (W == nullptr) return SGEMM_MI355_ERR_NULL;
+  if (((uintptr_t)W & 15) != 0) return SGEMM_MI355_ERR_ALIGN;
+  if ((uint64_t)w_bytes < need) return SGEMM_MI355_ERR_WORKSPACE;
+  if (workspace_overlaps(p, C, W, need)) return SGEMM_MI355_ERR_ALIAS;
+  plan.partials = W;
+  const GemmArgs g{p.M, p.N, p.K, p.A, p.lda, p.B, p.ldb, C, p.ldc, p.alpha, p.beta, 0, 0, 0, 1, p.K};
+  return cfg->streamk(g, plan, grid, direct, stream) == hipSuccess ? SGEMM_MI355_OK : SGEMM_MI355_ERR_LAUNCH;
+}
+
+// Stream-K selection. Each stream-K configuration of the op pair whose direct
+// kernel would run (the register-staged stream-K kernels were slower than the
+// plain path on every shape measured) and that leaves a partial last round is
+// predicted as its measured time per slab (the table's stream-K block) times
+// tiles * slabs / kCompute, plus kStreamKOverheadUs: the partial sums, two
+// BM x BN blocks per workgroup of the grid (occupancy x BM x BN is the same
+// for every stream-K tile, 128 MiB on 256 compute units), the fixup kernel
+// and its launch. The plain path's time is the larger of the nearest-shape
+// and the median estimates for the configuration it would run: rescaled from
+// a measured shape with a different fill, the first can be optimistic
+// (1280 x 1280 x 32768: 0.71 ms predicted, 1.13 ms measured). Stream-K is
+// chosen when it is predicted below kStreamKGain of that; otherwise -1.
+constexpr double kStreamKOverheadUs = 40.0;
+constexpr double kStreamKGain = 0.97;
+
+// The median model's estimate for configuration `id` (0 if the table has none).
+double global_estimate(int opA, int opB, int id, int M, int N, int K) {
+  const ResolvedBlock& rb = resolved().block[opA][opB];
+  for (size_t c = 0; c < rb.gid.size(); ++c)
+    if (rb.gid[c] == id) return rb.gnorm[c] * busy_time(*config_at(id), rb.gocc[c], M, N, K, 1);
+  return 0.0;
+}
+
+int select_streamk(int opA, int opB, int M, int N, int K, bool aligned) {
+  if (M <= 0 || N <= 0 || K <= 0) return -1;
+  double plain_us = 0.0;
+  int plain = model_select(opA, opB, M, N, K, aligned, &plain_us);
+  if (plain >= 0) {
+    const double g = global_estimate(opA, opB, plain, M, N, K);
+    if (g > plain_us) plain_us = g;
+  } else {
+    plain = global_select(opA, opB, M, N, K, 1, aligned, &plain_us);
+  }
+  if (plain < 0) return -1;
+  const ResolvedBlock& rb = resolved().block[opA][opB];
+  int best = -1;
+  double best_t = 0.0;
+  for (size_t c = 0; c < rb.skid.size(); ++c) {
+    const int id = rb.skid[c];
+    const KernelConfig& cfg = *config_at(id);
+    if (!direct_path(cfg, M, N, K, aligned)) continue;
+    const int64_t tiles = tiles_for(cfg, M, N);
+    if (tiles % ((int64_t)kCompute * rb.skocc[c]) == 0) continue;  // whole rounds: nothing to split
+    const double slabs = (double)tiles * (double)(((int64_t)K + cfg.bk - 1) / cfg.bk) / kCompute;
+    const double t = rb.sknorm[c] * slabs + kStreamKOverheadUs;
+    if (best < 0 || t < best_t) {
+      best = id;
+      best_t = t;
+    }
+  }
+  return (best >= 0 && best_t < kStreamKGain * plain_us) ? best : -1;
+}
+
 Problem plain(int M, int N, int K, const float* A, int lda, const float* B, int ldb, const float* C,
               int ldc) {
   return Problem{0, 0, M, N, K, 1.0f, A, lda, 0, B, ldb, 0, 0.0f, C, ldc, 0, 1};
@@ -633,6 +801,56 @@ int sgemm_mi355_select_splitk(int opA, int opB, int M, int N, int K, int* splits
   return SGEMM_MI355_OK;
 }
 
+size_t sgemm_mi355_streamk_workspace_size(int opA, int opB, int M, int N, int K, int config) {
+  if ((opA != 0 && opA != 1) || (opB != 0 && opB != 1) || M <= 0 || N <= 0 || K <= 0) return 0;
+  uint64_t need = 0;
+  if (config >= 0) {
+    const KernelConfig* c = config_at(config);
+    if (c && c->streamk && c->transA == opA && c->transB == opB) need = streamk_need(*c, M, N, K);
+  } else {
+    for (int aligned = 0; aligned < 2; ++aligned) {  // the choice may depend on alignment
+      const int id = select_streamk(opA, opB, M, N, K, aligned != 0);
+      if (id >= 0) {
+        const uint64_t n = streamk_need(*config_at(id), M, N, K);
+        if (n > need) need = n;
+      }
+    }
+  }
+  return (size_t)need;
+}
+
+int sgemm_mi355_streamk(int opA, int opB, int M, int N, int K, float alpha, const float* A, int lda,
+                        const float* B, int ldb, float beta, float* C, int ldc, float* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  const Problem p{opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1};
+  const int v = validate(p);
+  if (v != SGEMM_MI355_OK) return v;
+  const int id = select_streamk(opA, opB, M, N, K, operands_aligned(p));
+  return id >= 0 ? run_streamk(p, C, workspace, workspace_bytes, stream, id) : run(p, C, stream, select_for(p));
+}
+
+int sgemm_mi355_streamk_with_config(int opA, int opB, int M, int N, int K, float alpha,
+                                    const float* A, int lda, const float* B, int ldb, float beta,
+                                    float* C, int ldc, float* workspace, size_t workspace_bytes,
+                                    hipStream_t stream, int config) {
+  const Problem p{opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1};
+  return run_streamk(p, C, workspace, workspace_bytes, stream, config);
+}
+
+int sgemm_mi355_select_streamk(int opA, int opB, int M, int N, int K, int* config) {
+  if ((opA != 0 && opA != 1) || (opB != 0 && opB != 1)) return SGEMM_MI355_ERR_OP;
+  if (M < 0 || N < 0 || K < 0) return SGEMM_MI355_ERR_DIM;
+  if (!config) return SGEMM_MI355_ERR_NULL;
+  *config = select_streamk(opA, opB, M, N, K, true);
+  return SGEMM_MI355_OK;
+}
+
+int sgemm_mi355_config_streamk(int config) {
+  const KernelConfig* c = config_at(config);
+  if (!c) return SGEMM_MI355_ERR_CONFIG;
+  return c->streamk != nullptr ? 1 : 0;
+}
+
 int sgemm_mi355_validate(int M, int N, int K, const float* A, int lda, const float* B, int ldb,
                          const float* C, int ldc) {
   return validate(plain(M, N, K, A, lda, B, ldb, C, ldc));
@@ -720,11 +938,12 @@ const char* sgemm_mi355_strerror(int code) {
     case SGEMM_MI355_ERR_ALIGN: return "a matrix pointer is not 4-byte aligned";
     case SGEMM_MI355_ERR_STRIDE: return "a batch stride is negative, or batch entries of C overlap";
     case SGEMM_MI355_ERR_OP: return "an operand op is neither SGEMM_MI355_OP_N nor SGEMM_MI355_OP_T";
-    case SGEMM_MI355_ERR_WORKSPACE: return "the split-K workspace is smaller than sgemm_mi355_splitk_workspace_size";
+    case SGEMM_MI355_ERR_WORKSPACE:
+      return "the workspace is smaller than sgemm_mi355_splitk_workspace_size or sgemm_mi355_streamk_workspace_size";
     default: return "unknown error code";
   }
 }
 
-const char* sgemm_mi355_version(void) { return "0.5.0"; }
+const char* sgemm_mi355_version(void) { return "0.6.0"; }
 
 }  // extern "C"

@@ -29,6 +29,27 @@ struct GemmArgs {
 
 using LaunchFn = hipError_t (*)(const GemmArgs&, hipStream_t);
 
+// Stream-K schedule of one single-product launch on a persistent grid of G
+// workgroups. Tiles are numbered in the order of tile_coords. Tiles
+// [0, dp_tiles) run whole, tile j on workgroup j % G; the iters BK-deep slabs
+// of each of the sk_tiles tiles after them, sk_iters = sk_tiles * iters in
+// all, taken in tile order and ascending k, are dealt to the workgroups in
+// contiguous ranges, workgroup w taking [w * sk_iters / G, (w+1) * sk_iters / G).
+// A workgroup stores a piece of a tile that is not the whole tile as a dense
+// row-major BM x BN block of partial sums: in block 2w of `partials` if the
+// piece starts its range, else in block 2w + 1 (the piece that ends it).
+struct StreamKPlan {
+  int dp_tiles, sk_tiles;
+  int iters;
+  int64_t sk_iters;
+  float* partials;  // 2 * G blocks of BM * BN floats, 16-byte aligned
+};
+
+// Runs the stream-K kernel (grid G, direct loads when `direct`) and then the
+// kernel that adds the partial sums of every split tile into C.
+using StreamKLaunchFn = hipError_t (*)(const GemmArgs&, const StreamKPlan&, int grid, bool direct,
+                                       hipStream_t);
+
 enum KernelKind { KIND_MFMA = 0, KIND_VALU = 1 };
 
 struct KernelConfig {
@@ -40,6 +61,10 @@ struct KernelConfig {
   LaunchFn launch;
   const void* kernel;  // the kernel launch() runs for 16-byte aligned operands (occupancy queries)
   int kgroups;         // wave groups that split each slab's k range (1: none)
+  // Stream-K form (null where the configuration has none) and its two kernels,
+  // staged through registers [0] and by direct loads [1] (occupancy queries).
+  StreamKLaunchFn streamk;
+  const void* streamk_kernel[2];
 };
 
 // Host-only tables (not const: a const global would also be emitted for the

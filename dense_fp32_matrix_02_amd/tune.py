@@ -52,7 +52,10 @@ TABLE_HEADER = """\
 // {cut}x the shape's best (never a candidate there). Then every
 // configuration of the op pair with its occupancy and its median time per
 // unit of modelled busy time over the shapes: the selection's estimate for
-// batches and for problems with no measured shape nearby. A last block records,
+// batches and for problems with no measured shape nearby. Where stream-K forms
+// were timed (a grid of shapes whose tiles leave a partial last round), each
+// one's time per slab of the evenly dealt work beyond a fixed overhead,
+// median over those shapes (sgemm_mi355_select_streamk). A last block records,
 // per shape of a second grid, the fastest split count of sgemm_mi355_splitk,
 // which sgemm_mi355_select_splitk suggests for shapes near it.
 //
@@ -68,6 +71,18 @@ OPS_NAMES = ("nn", "nt", "tn", "tt")
 # The split-K grid: shapes whose tile grids leave compute units idle, and K
 # long enough for splitting to be worth a second pass.
 SPLIT_SIDES = (64, 96, 128, 192, 256, 384, 512, 768, 1024, 1536, 2048, 3072)
+# The stream-K grid: single products whose tile counts leave a partial last
+# round for every stream-K tile (M, N multiples of 4 and K of 16, so every op
+# pair takes the direct path), from long K on small M x N to large cubes.
+STREAMK_SHAPES = ((5120, 5120, 5120), (6144, 6144, 6144), (3072, 3072, 8192), (10240, 10240, 2048),
+                  (4608, 4608, 4608), (2560, 2560, 8192), (3328, 3328, 8192), (7168, 7168, 4096),
+                  (2048, 2048, 8192), (2048, 2048, 4096), (1536, 1536, 16384), (1024, 1024, 16384),
+                  (2048, 2048, 2048), (768, 768, 65536), (3584, 3584, 3584), (2816, 2816, 5632),
+                  (4352, 4352, 2048), (1280, 1280, 32768), (5120, 2560, 6144))
+# Fixed cost of a stream-K call beyond its slabs (kStreamKOverheadUs in
+# sgemm_api.hip): the partial sums (two BM x BN blocks per workgroup, 128 MiB
+# for every stream-K tile on 256 compute units), the fixup kernel and its launch.
+STREAMK_OVERHEAD_US = 40.0
 SPLIT_KS = (1024, 2048, 4096, 8192, 16384, 32768, 65536)
 
 
@@ -141,6 +156,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kinds", default="mfma", help="mfma, valu or mfma,valu")
     ap.add_argument("--splitk", default="", help="split counts to time with sgemm_mi355_splitk, e.g. 2,4,8")
+    ap.add_argument("--streamk", action="store_true",
+                    help="also time the stream-K form of every configuration that has one")
+    ap.add_argument("--streamk-grid", action="store_true",
+                    help="time plain and stream-K forms on the stream-K grid (for --table)")
     ap.add_argument("--splitk-grid", action="store_true",
                     help="time split counts 1..64 on the grid M, N in {64..3072} (powers of two and 1.5x them) x K in {1024..65536} "
                          "(powers of two) for the table's split-K block (no per-configuration timings)")
@@ -166,6 +185,11 @@ def main(argv=None):
         args.kinds = "none"
         args.splitk = "1,2,4,8,16,32,64"
         args.shapes = ",".join(f"{m}x{n}x{k}" for m in SPLIT_SIDES for n in SPLIT_SIDES for k in SPLIT_KS)
+    if args.streamk_grid:
+        if args.batch != 1 or args.grid:
+            ap.error("--streamk-grid times single products on its own grid")
+        args.streamk = True
+        args.shapes = ",".join(f"{m}x{n}x{k}" for m, n, k in STREAMK_SHAPES)
     if args.from_json:
         results = []
         for path in args.from_json.split(","):
@@ -191,13 +215,26 @@ def main(argv=None):
     for (M, N, K) in shapes:
         Ad, Bd, C = make_inputs(M, N, K, opA, opB, args.batch)
         row = {"M": M, "N": N, "K": K, "ops": args.ops, "batch": args.batch, "times_ms": {},
-               "occupancy": occupancy}
+               "occupancy": occupancy, "streamk_grid": bool(args.streamk_grid)}
         flops = 2 * M * N * K * args.batch
         for cid in cands:
             ms = time_call(config_call(Ad, Bd, C, cid, opA, opB, args.batch), args.reps, args.warmup)
             row["times_ms"][names[cid]] = ms
             print(f"{M}x{N}x{K}{tag} {names[cid]:28s} {ms:9.4f} ms {flops / ms / 1e9:9.2f} TFLOP/s",
                   flush=True)
+        if args.streamk and args.batch == 1:
+            for cid in [c for c in cands if sg.sgemm_mi355_config_streamk(c) == 1]:
+                need = sg.sgemm_mi355_streamk_workspace_size(opA, opB, M, N, K, cid)
+                ws = torch.empty((need + 3) // 4 + 4, device="cuda")
+                ms = time_call(lambda stream, cid=cid: sg.gemm_streamk(Ad, Bd, C, opA=opA, opB=opB, workspace=ws,
+                                                                       config=cid, stream=stream),
+                               args.reps, args.warmup)
+                row.setdefault("streamk_ms", {})[names[cid]] = ms
+                print(f"{M}x{N}x{K}{tag} streamk {names[cid]:28s} {ms:9.4f} ms {flops / ms / 1e9:9.2f} TFLOP/s",
+                      flush=True)
+                del ws
+            sel = sg.sgemm_mi355_select_streamk(opA, opB, M, N, K)
+            row["streamk_choice"] = names[sel] if sel >= 0 else None
         for sp in [int(x) for x in args.splitk.split(",") if x]:
             need = sg.sgemm_mi355_splitk_workspace_size(M, N, K, sp)
             ws = torch.empty((need + 3) // 4 + 1, device="cuda")
@@ -245,6 +282,32 @@ def config_geometry(name):
     return bm, bn, bk, int(kg.group(1)) if kg else 1
 
 
+def streamk_norms(rows, occ):
+    """{name: (occupancy, microseconds per slab)} for the stream-K forms timed
+    in `rows`: per configuration, the median over shapes where its direct
+    kernel splits tiles of (time - STREAMK_OVERHEAD_US) / (tiles * slabs / 256)."""
+    import dense_fp32_matrix_02_amd as sg
+
+    known = set(sg.config_names())
+    per = {}
+    for r in rows:
+        M, N, K = r["M"], r["N"], r["K"]
+        for n, ms in r["streamk_ms"].items():
+            if n not in known or n not in occ:
+                continue
+            cid = sg.config_id(n)
+            bm, bn, bk, _ = sg.sgemm_mi355_config_info(cid)
+            opA, opB = sg.sgemm_mi355_config_ops(cid)
+            if K % bk or (opA and M % 4) or (not opB and N % 4):
+                continue  # register-staged kernel
+            tiles = -(-M // bm) * -(-N // bn)
+            if tiles % (256 * occ[n]) == 0:
+                continue  # whole rounds: the plain launch ran
+            slabs = tiles * -(-K // bk) / 256
+            per.setdefault(n, []).append((ms * 1e3 - STREAMK_OVERHEAD_US) / slabs)
+    return {n: (occ[n], statistics.median(v)) for n, v in sorted(per.items())}
+
+
 def write_table(results, path, reps):
     """The tile table from single-product rows of any op pairs: per op pair,
     the configurations that are fastest on at least one shape, their
@@ -258,7 +321,9 @@ def write_table(results, path, reps):
         f.write(TABLE_HEADER.format(reps=reps, cut=TABLE_CUT))
         blocks = []
         for ops in OPS_NAMES:
-            rows = [r for r in results if r.get("ops", "nn") == ops and r.get("batch", 1) == 1]
+            sk_rows = [r for r in results if r.get("ops", "nn") == ops and r.get("streamk_ms")]
+            rows = [r for r in results if r.get("ops", "nn") == ops and r.get("batch", 1) == 1
+                    and not r.get("streamk_grid")]
             rows = [r for r in rows if any(n.startswith("mfma") for n in r["times_ms"])]
             if not rows:
                 continue
@@ -301,7 +366,15 @@ def write_table(results, path, reps):
                           for r in rows if n in r["times_ms"]]
                 f.write(f'    {{"{n}", {occ[n]}, {statistics.median(ratios):.5g}}},\n')
             f.write("};\n")
-            blocks.append((ops, len(cands), len(rows), len(names)))
+            # stream-K: each configuration's time per slab of the evenly dealt
+            # work, beyond the fixed overhead, median over the measured shapes
+            sk = streamk_norms(sk_rows, occ)
+            if sk:
+                f.write(f"static const TableNorm kStreamK_{ops}[] = {{\n")
+                for n, (o, us) in sk.items():
+                    f.write(f'    {{"{n}", {o}, {us:.5g}}},\n')
+                f.write("};\n")
+            blocks.append((ops, len(cands), len(rows), len(names), len(sk)))
         split_rows = [r for r in results if r.get("splitk_ms") and r.get("batch", 1) == 1
                       and r.get("ops", "nn") == "nn"]
         f.write("\n// split-K: per measured shape {M, N, K, fastest split count} among 1, 2, 4, ..., 64\n")
@@ -311,9 +384,9 @@ def write_table(results, path, reps):
             f.write(f'    {{{r["M"]}, {r["N"]}, {r["K"]}, {min(t, key=t.get)}}},\n')
         f.write("    {0, 0, 0, 0},  // sentinel\n};\n")
         f.write("\nstatic const TableBlock kTableBlocks[] = {\n")
-        for ops, nc, nr, nn in blocks:
+        for ops, nc, nr, nn, ns in blocks:
             f.write(f"    {{{int(ops[0] == 't')}, {int(ops[1] == 't')}, {nc}, {nr}, kCand_{ops}, kShapes_{ops}, "
-                    f"kTimes_{ops}, {nn}, kNorm_{ops}}},\n")
+                    f"kTimes_{ops}, {nn}, kNorm_{ops}, {ns}, {f'kStreamK_{ops}' if ns else 'nullptr'}}},\n")
         f.write("};\n")
 
 

@@ -60,7 +60,7 @@ extern "C" {
 #define SGEMM_MI355_ERR_ALIGN (-8)    /* a pointer is not 4-byte aligned */
 #define SGEMM_MI355_ERR_STRIDE (-9)   /* a batch stride is negative, or batch entries of C overlap */
 #define SGEMM_MI355_ERR_OP (-10)      /* an op argument is neither OP_N nor OP_T */
-#define SGEMM_MI355_ERR_WORKSPACE (-11) /* split-K workspace smaller than required */
+#define SGEMM_MI355_ERR_WORKSPACE (-11) /* split-K or stream-K workspace smaller than required */
 
 /* Operand ops for the general entry points (row-major storage throughout). */
 #define SGEMM_MI355_OP_N 0 /* op(X) = X */
@@ -203,6 +203,68 @@ int sgemm_mi355_splitk_with_config(int opA, int opB, int M, int N, int K, float 
  * bad arguments.
  */
 int sgemm_mi355_select_splitk(int opA, int opB, int M, int N, int K, int *splits, int *config);
+
+/*
+ * Stream-K form of sgemm_mi355_ex (single products), for large problems whose
+ * tile count leaves the last round of workgroups thin (the work-centric
+ * decomposition of Osama et al., PPoPP 2023). A persistent grid of
+ * (compute units x occupancy) workgroups runs the whole rounds of block tiles
+ * as sgemm_mi355_ex does, and deals the BK-deep slabs of the remaining tiles
+ * out evenly, in contiguous ranges that cross tile boundaries. A tile split
+ * between workgroups leaves dense BM x BN blocks of partial sums in
+ * `workspace`; a second kernel adds them in ascending k order and sets
+ * C = alpha * sum + beta * C. The order is fixed, so repeated calls on one
+ * device give identical bits; the result rounds differently from the unsplit
+ * product but stays within the same error bound, and integer-valued products
+ * are exact.
+ *
+ * The library picks the configuration with a model of the measured table
+ * (sgemm_mi355_select_streamk) and runs the plain sgemm_mi355_ex path where
+ * stream-K is not predicted to pay. `workspace` is device memory owned by the
+ * caller, at least sgemm_mi355_streamk_workspace_size(opA, opB, M, N, K, -1)
+ * bytes (it depends on the current device's compute units), 16-byte aligned,
+ * not overlapping A, B or C; it may be NULL when that size is 0. Both kernels
+ * are enqueued on `stream`; the workspace may be reused once work ordered
+ * after them on that stream starts. A short workspace gives
+ * SGEMM_MI355_ERR_WORKSPACE, a misaligned one SGEMM_MI355_ERR_ALIGN; the
+ * other errors are those of sgemm_mi355_ex.
+ */
+int sgemm_mi355_streamk(int opA, int opB, int M, int N, int K, float alpha,
+                        const float *A, int lda, const float *B, int ldb,
+                        float beta, float *C, int ldc,
+                        float *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sgemm_mi355_streamk with configuration `config`, which must have a
+ * stream-K form (sgemm_mi355_config_streamk) built for this opA/opB pair,
+ * else SGEMM_MI355_ERR_CONFIG. When the tiles fill whole rounds of the grid,
+ * nothing is split: it runs the plain launch of `config` and needs no
+ * workspace. For tuning and tests.
+ */
+int sgemm_mi355_streamk_with_config(int opA, int opB, int M, int N, int K, float alpha,
+                                    const float *A, int lda, const float *B, int ldb,
+                                    float beta, float *C, int ldc,
+                                    float *workspace, size_t workspace_bytes,
+                                    hipStream_t stream, int config);
+
+/*
+ * Workspace bytes the stream-K call needs on the current device: for
+ * configuration `config`, or with config = -1 for the library's own choice
+ * (either operand alignment). Two BM x BN FP32 blocks per workgroup of the
+ * grid (128 MiB for 256 x 256 tiles on 256 compute units); 0 when no tile
+ * is split, or for invalid arguments.
+ */
+size_t sgemm_mi355_streamk_workspace_size(int opA, int opB, int M, int N, int K, int config);
+
+/*
+ * The configuration sgemm_mi355_streamk would run in stream-K form for
+ * 16-byte aligned operands, or -1 when it would take the plain path (host
+ * only). Returns 0, or SGEMM_MI355_ERR_OP / _DIM / _NULL.
+ */
+int sgemm_mi355_select_streamk(int opA, int opB, int M, int N, int K, int *config);
+
+/* 1 if configuration `config` has a stream-K form, 0 if not, or SGEMM_MI355_ERR_CONFIG. */
+int sgemm_mi355_config_streamk(int config);
 
 /*
  * Argument validation alone: returns the code the entry points above would

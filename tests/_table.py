@@ -68,3 +68,15 @@ def read_norms(path: str = TABLE_PATH):
             out[pair] = [(n, int(o), float(np.float32(v)))
                          for n, o, v in re.findall(r'\{"([^"]+)", (\d+), ([0-9.eE+-]+)\}', m.group(1))]
     return out
+
+
+def read_streamk(path: str = TABLE_PATH):
+    """{(opA, opB): [(name, occupancy, microseconds per slab)]}: the stream-K block."""
+    text = open(path).read()
+    out = {}
+    for ops, pair in OP_PAIRS.items():
+        m = re.search(r"kStreamK_%s\[\] = \{(.*?)\n\};" % ops, text, re.S)
+        if m:
+            out[pair] = [(n, int(o), float(np.float32(v)))
+                         for n, o, v in re.findall(r'\{"([^"]+)", (\d+), ([0-9.eE+-]+)\}', m.group(1))]
+    return out

@@ -177,6 +177,33 @@ int main() {
                                    ws - 4, stream),
                 SGEMM_MI355_ERR_WORKSPACE);
   }
+  {  // stream-K in 256x256 tiles: 9 tiles whose slabs are dealt to the whole grid,
+     // partial sums added by the fixup kernel; the same bits on a second call
+    const int M = 600, N = 520, K = 1040;
+    int cid = -1;
+    for (int i = 0; i < sgemm_mi355_num_configs(); ++i)
+      if (std::strcmp(sgemm_mi355_config_name(i), "mfma32_256x256x16_w4x4_lds2") == 0) cid = i;
+    Ints g(6);
+    std::vector<float> A = g.fill((size_t)M * K), B = g.fill((size_t)K * N);
+    std::vector<float> C0 = g.fill((size_t)M * N), want = C0;
+    const size_t ws = cid < 0 ? 0 : sgemm_mi355_streamk_workspace_size(0, 0, M, N, K, cid);
+    Dev dA(A), dB(B), dC(C0), dW(ws / sizeof(float) + 4);
+    int rc = cid < 0 || ws == 0 ? SGEMM_MI355_ERR_CONFIG
+                                : sgemm_mi355_streamk_with_config(0, 0, M, N, K, 3.0f, dA.p, K, dB.p, N, 0.5f, dC.p,
+                                                                  N, dW.p, ws, stream, cid);
+    HIP_OK(hipStreamSynchronize(stream));
+    ref_sgemm_ex_f32(0, 0, M, N, K, 3.0f, A.data(), K, B.data(), N, 0.5f, want.data(), N);
+    check("sgemm_mi355_streamk_with_config 600x520x1040, alpha=3 beta=0.5", rc, dC.get(), want);
+    dC.put(C0);
+    rc = sgemm_mi355_streamk_with_config(0, 0, M, N, K, 3.0f, dA.p, K, dB.p, N, 0.5f, dC.p, N, dW.p, ws, stream,
+                                         cid);
+    HIP_OK(hipStreamSynchronize(stream));
+    check("sgemm_mi355_streamk repeated call", rc, dC.get(), want);
+    expect_code("sgemm_mi355_streamk short workspace",
+                sgemm_mi355_streamk_with_config(0, 0, M, N, K, 3.0f, dA.p, K, dB.p, N, 0.5f, dC.p, N, dW.p,
+                                                ws - 16, stream, cid),
+                SGEMM_MI355_ERR_WORKSPACE);
+  }
   {  // argument errors are reported before anything is enqueued
     Dev d(64 * 64);
     expect_code("negative M", sgemm_mi355(-1, 4, 4, d.p, 4, d.p, 4, d.p, 4, stream), SGEMM_MI355_ERR_DIM);

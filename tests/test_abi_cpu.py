@@ -381,11 +381,12 @@ def _direct_path(name, M, N, K):
     return M > 0 and N > 0 and K > 0 and K % bk == 0 and (not opA or M % 4 == 0) and (opB or N % 4 == 0)
 
 
-def _model_select(blocks, opA, opB, M, N, K):
+def _model_predict(blocks, opA, opB, M, N, K):
     """The measured shape nearest (M, N, K) in summed |log2| distance among
     those within a factor of two in each dimension (first on a tie), then the
     candidate whose time there, scaled by the busy-time ratio, is least
-    (first on a tie); None when no measured shape qualifies."""
+    (first on a tie): (predicted microseconds, name), or None when no
+    measured shape qualifies."""
     import math
     cands, shapes, times = blocks[(opA, opB)]
     near = None
@@ -410,6 +411,11 @@ def _model_select(blocks, opA, opB, M, N, K):
         pred = t / _busy(cid, occ, m, n, k) * _busy(cid, occ, M, N, K)
         if best is None or pred < best[0]:
             best = (pred, name)
+    return best
+
+
+def _model_select(blocks, opA, opB, M, N, K):
+    best = _model_predict(blocks, opA, opB, M, N, K)
     return best[1] if best else None
 
 
@@ -454,11 +460,11 @@ def test_model_selection_matches_its_definition():
     assert checked > 500
 
 
-def _global_select(norms, opA, opB, M, N, K, batch):
+def _global_predict(norms, opA, opB, M, N, K, batch):
     """Every configuration of the op pair, predicted as its median time per
     busy unit times the busy time of this problem (batch entries included);
-    the least wins (first on a tie). Direct-to-LDS configurations count only
-    on their direct path."""
+    the least wins (first on a tie): (predicted microseconds, name).
+    Direct-to-LDS configurations count only on their direct path."""
     best = None
     for name, occ, us in norms[(opA, opB)]:
         if "_lds" in name and not _direct_path(name, M, N, K):
@@ -466,7 +472,11 @@ def _global_select(norms, opA, opB, M, N, K, batch):
         t = us * _busy(_id(name), occ, M, N, K, batch)
         if best is None or t < best[0]:
             best = (t, name)
-    return best[1]
+    return best
+
+
+def _global_select(norms, opA, opB, M, N, K, batch):
+    return _global_predict(norms, opA, opB, M, N, K, batch)[1]
 
 
 def test_median_model_selection_matches_its_definition():
@@ -514,3 +524,86 @@ def test_tuner_busy_time_is_the_selections():
         M, N, K, batch = rng.randint(1, 20000), rng.randint(1, 20000), rng.randint(1, 70000), rng.randint(1, 300)
         want = _busy(_id(name), occ, M, N, K, batch)
         assert tune.busy_time(*tune.config_geometry(name), occ, M, N, K, batch) == pytest.approx(want, rel=1e-12)
+
+
+STREAMK_OVERHEAD_US = 40.0  # fixed cost of a stream-K call in the selection model
+STREAMK_GAIN = 0.97         # stream-K is chosen below this fraction of the plain estimate
+
+
+def _streamk_select(blocks, norms, sk, opA, opB, M, N, K):
+    """Stream-K selection for aligned operands, written out: the plain path's
+    estimate is the larger of the nearest-shape prediction and the median
+    model's for the configuration the plain path runs (the median model's
+    own choice when no measured shape is near); each stream-K configuration
+    on its direct path whose tiles leave a partial last round of 256 x
+    occupancy workgroups is predicted as its time per slab x tiles x slabs /
+    256 + STREAMK_OVERHEAD_US; the least wins (first on a tie) if it is below
+    STREAMK_GAIN of the plain estimate. Returns a name or None."""
+    import math
+    plain = _model_predict(blocks, opA, opB, M, N, K)
+    if plain is not None:
+        est, name = plain
+        for n, occ, us in norms[(opA, opB)]:
+            if n == name:
+                est = max(est, us * _busy(_id(n), occ, M, N, K))
+    else:
+        est, name = _global_predict(norms, opA, opB, M, N, K, 1)
+    best = None
+    for n, occ, us in sk.get((opA, opB), []):
+        if not _direct_path(n, M, N, K):
+            continue
+        bm, bn, bk, _ = sg.sgemm_mi355_config_info(_id(n))
+        tiles = math.ceil(M / bm) * math.ceil(N / bn)
+        if tiles % (256 * occ) == 0:
+            continue
+        t = us * (tiles * math.ceil(K / bk) / 256) + STREAMK_OVERHEAD_US
+        if best is None or t < best[0]:
+            best = (t, n)
+    return best[1] if best is not None and best[0] < STREAMK_GAIN * est else None
+
+
+def test_streamk_selection_matches_its_definition():
+    """sgemm_mi355_select_streamk (host only) is the rule above, for every op
+    pair, on the stream-K grid, on random shapes and on shapes with whole
+    rounds of tiles, a K tail or ragged lines (no direct path)."""
+    import random
+    from tests._table import read_norms, read_streamk
+    blocks, norms, sk = _table(), read_norms(), read_streamk()
+    assert set(sk) == set(OP_PAIRS.values())
+    names = sg.config_names()
+    rng = random.Random(11)
+    chosen = plain = 0
+    for (opA, opB) in OP_PAIRS.values():
+        cases = [(5120, 5120, 5120), (4608, 4608, 4608), (1280, 1280, 32768), (8192, 8192, 8192),
+                 (4096, 4096, 4096), (5120, 5120, 5121), (5122, 5120, 5120), (5120, 5122, 5120), (3001, 2047, 1537)]
+        cases += [(4 * rng.randint(16, 4096), 4 * rng.randint(16, 4096), 16 * rng.randint(8, 4096)) for _ in range(120)]
+        cases += [(rng.randint(64, 16384), rng.randint(64, 16384), rng.randint(128, 65536)) for _ in range(40)]
+        for M, N, K in cases:
+            want = _streamk_select(blocks, norms, sk, opA, opB, M, N, K)
+            got = sg.sgemm_mi355_select_streamk(opA, opB, M, N, K)
+            assert (names[got] if got >= 0 else None) == want, (opA, opB, M, N, K)
+            chosen += want is not None
+            plain += want is None
+        assert sg.sgemm_mi355_select_streamk(opA, opB, 8192, 8192, 8192) == -1  # whole rounds
+    assert chosen > 100 and plain > 100
+
+
+def test_streamk_table_and_errors():
+    """The stream-K block names stream-K configurations of its op pair with
+    positive times; the selection's argument errors."""
+    from tests._table import read_streamk
+    for pair, rows in read_streamk().items():
+        assert len(rows) == 4
+        for name, occ, us in rows:
+            cid = _id(name)
+            assert sg.sgemm_mi355_config_streamk(cid) == 1 and sg.sgemm_mi355_config_ops(cid) == pair
+            assert occ >= 1 and 0.5 < us < 10.0
+    assert sg.sgemm_mi355_config_streamk(10 ** 6) == sg.ERR_CONFIG
+    with pytest.raises(sg.SgemmError):
+        sg.sgemm_mi355_select_streamk(2, 0, 64, 64, 64)
+    with pytest.raises(sg.SgemmError):
+        sg.sgemm_mi355_select_streamk(0, 0, -1, 64, 64)
+    assert sg.sgemm_mi355_select_streamk(0, 0, 0, 64, 64) == -1
+    # arguments that describe no product need no workspace
+    assert sg.sgemm_mi355_streamk_workspace_size(0, 0, 0, 64, 64, -1) == 0
+    assert sg.sgemm_mi355_streamk_workspace_size(3, 0, 64, 64, 64, -1) == 0

@@ -1,5 +1,6 @@
 """The entry points under HIP graph capture: every launch the library makes
-(the GEMM kernels, the split-K reduction, the C = beta*C kernel for K == 0)
+(the GEMM kernels, the split-K reduction, the stream-K kernel and its fixup,
+the C = beta*C kernel for K == 0)
 is an ordinary kernel node, with no memset node, so a captured call can be
 replayed. Each case captures one call, then replays it several times with
 unrelated eager work and synchronisations between the replays, refilling C
@@ -96,6 +97,25 @@ def test_graph_splitk_two_kernels():
     graph = _capture(lambda: sg.gemm_splitk(Ad, Bd, C, splits=splits, workspace=ws))
     nan = torch.full((M, N), float("nan"), device="cuda")
     _replay_and_check(graph, C, nan, oracle.sgemm_f32(A, B), "split-K")
+
+
+def test_graph_streamk_two_kernels():
+    """Stream-K in 256x256 tiles: 25 tiles whose slabs are dealt to the whole
+    grid, then the fixup kernel adds the partial sums (alpha 2, beta -1)."""
+    M, N, K = 1280, 1280, 2048
+    A, B = _ints(M, K, 8), _ints(K, N, 9)
+    C0 = _ints(M, N, 10)
+    Ad, Bd = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    C = torch.empty((M, N), device="cuda")
+    cid = sg.config_id("mfma32_256x256x16_w4x4_lds2")
+    need = sg.sgemm_mi355_streamk_workspace_size(0, 0, M, N, K, cid)
+    assert need > 0
+    ws = torch.empty((need + 3) // 4, device="cuda")
+    C.copy_(torch.from_numpy(C0))
+    graph = _capture(lambda: sg.gemm_streamk(Ad, Bd, C, alpha=2.0, beta=-1.0, workspace=ws, config=cid))
+    want = C0.copy()
+    oracle.sgemm_ex_f32(0, 0, 2.0, A, B, -1.0, want)
+    _replay_and_check(graph, C, torch.from_numpy(C0).cuda(), want, "stream-K")
 
 
 def test_graph_k_zero_fills_c():
