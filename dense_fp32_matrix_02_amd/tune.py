@@ -158,6 +158,8 @@ def main(argv=None):
     ap.add_argument("--splitk", default="", help="split counts to time with sgemm_mi355_splitk, e.g. 2,4,8")
     ap.add_argument("--streamk", action="store_true",
                     help="also time the stream-K form of every configuration that has one")
+    ap.add_argument("--selected", action="store_true",
+                    help="time only the configuration the library selects for each shape")
     ap.add_argument("--streamk-grid", action="store_true",
                     help="time plain and stream-K forms on the stream-K grid (for --table)")
     ap.add_argument("--splitk-grid", action="store_true",
@@ -210,20 +212,24 @@ def main(argv=None):
         sides = [128, 256, 512, 1024, 2048, 4096, 8192]
         shapes += [(m, n, k) for m in sides for n in sides for k in (256, 1024, 4096, 16384)
                    if (m, n, k) not in shapes]
-    occupancy = {names[cid]: sg.sgemm_mi355_config_occupancy(cid) for cid in cands}
+    # stream-K forms are timed whatever --kinds says
+    sk_cands = [i for i in range(len(names)) if sg.sgemm_mi355_config_streamk(i) == 1
+                and sg.sgemm_mi355_config_ops(i) == (opA, opB)] if args.streamk else []
+    occupancy = {names[cid]: sg.sgemm_mi355_config_occupancy(cid) for cid in cands + sk_cands}
     tag = ("" if args.ops == "nn" else f" {args.ops}") + ("" if args.batch == 1 else f" x{args.batch}")
     for (M, N, K) in shapes:
         Ad, Bd, C = make_inputs(M, N, K, opA, opB, args.batch)
         row = {"M": M, "N": N, "K": K, "ops": args.ops, "batch": args.batch, "times_ms": {},
                "occupancy": occupancy, "streamk_grid": bool(args.streamk_grid)}
         flops = 2 * M * N * K * args.batch
-        for cid in cands:
+        shape_cands = [sg.sgemm_mi355_select_config_ex(opA, opB, M, N, K, args.batch)] if args.selected else cands
+        for cid in shape_cands:
             ms = time_call(config_call(Ad, Bd, C, cid, opA, opB, args.batch), args.reps, args.warmup)
             row["times_ms"][names[cid]] = ms
             print(f"{M}x{N}x{K}{tag} {names[cid]:28s} {ms:9.4f} ms {flops / ms / 1e9:9.2f} TFLOP/s",
                   flush=True)
         if args.streamk and args.batch == 1:
-            for cid in [c for c in cands if sg.sgemm_mi355_config_streamk(c) == 1]:
+            for cid in sk_cands:
                 need = sg.sgemm_mi355_streamk_workspace_size(opA, opB, M, N, K, cid)
                 ws = torch.empty((need + 3) // 4 + 4, device="cuda")
                 ms = time_call(lambda stream, cid=cid: sg.gemm_streamk(Ad, Bd, C, opA=opA, opB=opB, workspace=ws,
