@@ -377,9 +377,8 @@ hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
 
 }  // namespace
 
-// Name: mfma32_<BM>x<BN>x<BK>_w<WM>x<WN>[_g8][_bk][_kg<KG>][_<ops>]: _g8 walks
-// the tile grid in bands of 8 tile rows instead of 4; _bk stages B (read
-// line-contiguous) k-major; _kg<KG> splits each slab's k range among KG wave
+// Name: mfma32_<BM>x<BN>x<BK>_w<WM>x<WN>[_bk][_kg<KG>][_<ops>]: _bk stages B
+// (read line-contiguous) k-major; _kg<KG> splits each slab's k range among KG wave
 // groups (see MfmaCfg); <ops> = tn, nt or tt names transposed operands (first
 // letter A, second B); no ops suffix is the plain product.
 #define SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, KG, GM, LA, LB, TA, TB, SUFFIX)                       \
@@ -387,7 +386,6 @@ hipError_t launch_mfma(const GemmArgs& g, hipStream_t stream) {
    64 * WM * WN * KG, TA, TB, &launch_mfma<MfmaCfg<BM, BN, BK, WM, WN, LA, LB, GM, KG>>,        \
    reinterpret_cast<const void*>(&mfma_gemm_kernel<MfmaCfg<BM, BN, BK, WM, WN, LA, LB, GM, KG>>), KG}
 #define SGEMM_MFMA_N(BM, BN, BK, WM, WN) SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, 1, 4, KC, MC, 0, 0, "")
-#define SGEMM_MFMA_G8(BM, BN, BK, WM, WN) SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, 1, 8, KC, MC, 0, 0, "_g8")
 #define SGEMM_MFMA_K(BM, BN, BK, WM, WN) SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, 1, 4, KC, KM, 0, 0, "_bk")
 #define SGEMM_MFMA_KG(BM, BN, BK, WM, WN, KG) \
   SGEMM_MFMA_CFG(BM, BN, BK, WM, WN, KG, 4, KC, MC, 0, 0, "_kg" #KG)
@@ -413,7 +411,6 @@ KernelConfig kMfmaConfigs[] = {
     SGEMM_MFMA_K(256, 128, 32, 2, 4),
     SGEMM_MFMA_N(256, 128, 16, 4, 2),
     SGEMM_MFMA_N(256, 128, 32, 4, 2),
-    SGEMM_MFMA_G8(256, 128, 16, 4, 2),
     // B staged k-major with 16 waves: 128-bit fragment reads for both operands
     SGEMM_MFMA_K(256, 256, 16, 4, 4),
     SGEMM_MFMA_K(256, 128, 16, 4, 2),
