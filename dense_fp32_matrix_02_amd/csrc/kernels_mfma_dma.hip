@@ -202,6 +202,241 @@ struct DmaCfg {
   static constexpr int WAVES_EU = LDS_WGS * NW / 4 < 4 ? (LDS_WGS * NW / 4 > 1 ? LDS_WGS * NW / 4 : 1) : 4;
 };
 
+// DIRECT: every slab by direct loads (the launcher guarantees 16-byte aligned
+// chunks inside the matrices and K a multiple of BK); otherwise every slab
+// through registers. Two kernels rather than a branch, so each gets the
+// registers it needs. The direct kernels are held to the registers of
+// WAVES_EU waves per SIMD (128 VGPRs for four), so small tiles keep several
+// workgroups per compute unit instead of spending the register file on one.
+template <class Cfg, bool DIRECT>
+__global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_kernel(GemmArgs g) {
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
+  constexpr int ST = Cfg::STAGES, NW = Cfg::NW;
+  using SA = typename Cfg::SlabA;
+  using SB = typename Cfg::SlabB;
+  // One array per stage, selected at compile time: the compiler can then see
+  // that a direct load into one stage does not alias reads of another, and
+  // does not make those reads wait for the load.
+  __shared__ __attribute__((aligned(1024))) float As0[SA::FLOATS];
+  __shared__ __attribute__((aligned(1024))) float As1[SA::FLOATS];
+  __shared__ __attribute__((aligned(1024))) float As2[ST > 2 ? SA::FLOATS : 4];
+  __shared__ __attribute__((aligned(1024))) float Bs0[SB::FLOATS];
+  __shared__ __attribute__((aligned(1024))) float Bs1[SB::FLOATS];
+  __shared__ __attribute__((aligned(1024))) float Bs2[ST > 2 ? SB::FLOATS : 4];
+  auto stage_a = [&](auto st) -> float* {
+    if constexpr (decltype(st)::value == 0) return As0;
+    else if constexpr (decltype(st)::value == 1) return As1;
+    else return As2;
+  };
+  auto stage_b = [&](auto st) -> float* {
+    if constexpr (decltype(st)::value == 0) return Bs0;
+    else if constexpr (decltype(st)::value == 1) return Bs1;
+    else return Bs2;
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+
+  const int M = g.M, N = g.N;
+  const int K = (blockIdx.y == gridDim.y - 1) ? g.k_last : g.K;  // last split-K chunk may be short
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int kg = Cfg::KG == 1 ? 0 : wave / (Cfg::WM * Cfg::WN);  // k group
+  const int wt = Cfg::KG == 1 ? wave : wave % (Cfg::WM * Cfg::WN);  // wave tile within the group
+  const int wm = wt % Cfg::WM, wn = wt / Cfg::WM;
+  const int l32 = lane & 31, h = lane >> 5;
+  const float* A = g.A + (int64_t)blockIdx.y * g.strideA;
+  const float* B = g.B + (int64_t)blockIdx.y * g.strideB;
+
+  // ---- direct loads: region q = p*NW + wave of each slab is this wave's ----
+  const float* a_src[SA::PER_WAVE];
+#pragma unroll
+  for (int p = 0; p < SA::PER_WAVE; ++p) a_src[p] = SA::direct_src(A, g.lda, m0, M, (p * NW + wave) * 64 + lane);
+  const float* b_src[SB::PER_WAVE];
+#pragma unroll
+  for (int p = 0; p < SB::PER_WAVE; ++p) b_src[p] = SB::direct_src(B, g.ldb, n0, N, (p * NW + wave) * 64 + lane);
+  auto issue_direct = [&](int k0, auto stage) {
+    float* as = stage_a(stage);
+    float* bs = stage_b(stage);
+    const int64_t oa = SA::k_offset(k0, g.lda), ob = SB::k_offset(k0, g.ldb);
+#pragma unroll
+    for (int p = 0; p < SA::PER_WAVE; ++p) copy16_to_lds(a_src[p] + oa, as + (p * NW + wave) * 256);
+#pragma unroll
+    for (int p = 0; p < SB::PER_WAVE; ++p) copy16_to_lds(b_src[p] + ob, bs + (p * NW + wave) * 256);
+  };
+
+  // ---- register staging (edge tiles, unaligned operands, the K tail) ------
+  f32x4 ra[SA::CHUNKS], rb[SB::CHUNKS];
+  auto load_regs = [&](int k0, bool tail) {
+    SA::load(ra, A, g.lda, m0, M, K, k0, tail, t);
+    SB::load(rb, B, g.ldb, n0, N, K, k0, tail, t);
+  };
+  auto store_regs = [&](auto stage) {
+    SA::store(stage_a(stage), ra, t);
+    SB::store(stage_b(stage), rb, t);
+  };
+
+  // ---- fragments and the inner product ------------------------------------
+  const int akey = SA::frag_key(l32, h), bkey = SB::frag_key(l32, h);
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Group kg multiplies k = kg*KSUB .. (kg+1)*KSUB - 1 of each slab; KSUB is a
+  // multiple of 32, so for k-contiguous slabs that offset commutes with the
+  // fragment swizzle.
+  const int kbase = kg * Cfg::KSUB;
+  auto compute = [&](auto stage) {
+    const float* as = SA::frag_base(stage_a(stage), wm * Cfg::WTM, l32, h) + SA::k_offset(kbase, BM);
+    const float* bs = SB::frag_base(stage_b(stage), wn * Cfg::WTN, l32, h) + SB::k_offset(kbase, BN);
+#pragma unroll
+    for (int kk = 0; kk < Cfg::KSUB; kk += 8) {
+      f32x4 af[FM], bf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = SA::frag(as, i, kk, akey);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bf[j] = SB::frag(bs, j, kk, bkey);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][u], bf[j][u], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // ---- K loop ---------------------------------------------------------------
+  const int nfull = K / BK;               // slabs with no k >= K
+  const bool tail = (K % BK) != 0;
+  if constexpr (DIRECT) {
+    // STAGES-deep pipeline of direct loads over the full slabs: slab s+ST-1 is
+    // in flight while slab s is multiplied (slab s lives in stage s % ST).
+    // Each wave waits for its own loads of the next slab, then the barrier
+    // publishes them to the workgroup. The loop is unrolled by ST so every
+    // stage index is a constant.
+    issue_direct(0, S0{});
+    if (ST > 2 && nfull > 1) issue_direct(BK, S1{});
+    wait_loads();
+    __syncthreads();
+    auto step = [&](auto cur, int s) {
+      constexpr int CUR = decltype(cur)::value;
+      using Next = std::integral_constant<int, (CUR + ST - 1) % ST>;
+      const bool more = s + ST - 1 < nfull;
+      if (more) issue_direct((s + ST - 1) * BK, Next{});
+      __builtin_amdgcn_sched_barrier(0);
+      compute(cur);
+      if constexpr (ST == 3) {
+        // Slab s+1 must have landed; slab s+2's loads may stay in flight.
+        constexpr int per_slab = SA::PER_WAVE + SB::PER_WAVE;
+        static_assert(per_slab <= 15, "vmcnt field");
+        if (more) __builtin_amdgcn_s_waitcnt(0x0F70 | per_slab);
+        else wait_loads();
+      } else {
+        wait_loads();
+      }
+      __syncthreads();
+    };
+    // Whole groups of ST slabs, then the remaining nfull % ST (no exit from
+    // the middle of the unrolled body, so the accumulators stay in place).
+    int s = 0;
+    for (; s + ST <= nfull; s += ST) {
+      step(S0{}, s);
+      step(S1{}, s + 1);
+      if constexpr (ST > 2) step(S2{}, s + 2);
+    }
+    if (s < nfull) step(S0{}, s);
+    if (s + 1 < nfull) step(S1{}, s + 1);
+  } else {
+    // Register staging through stages 0 and 1, last slab peeled.
+    const int nk = nfull + (tail ? 1 : 0);
+    load_regs(0, tail && nk == 1);
+    store_regs(S0{});
+    __syncthreads();
+    auto rstep = [&](auto cur, int s) {
+      using Other = std::integral_constant<int, 1 - decltype(cur)::value>;
+      if (s + 1 < nk) load_regs((s + 1) * BK, tail && s + 2 == nk);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(cur);
+      if (s + 1 < nk) store_regs(Other{});
+      __syncthreads();
+    };
+    int s = 0;
+    for (; s + 2 <= nk; s += 2) {
+      rstep(S0{}, s);
+      rstep(S1{}, s + 1);
+    }
+    if (s < nk) rstep(S0{}, s);
+  }
+
+  // ---- k groups: add the groups' sums in ascending group order ----------
+  if constexpr (Cfg::KG > 1) {
+    constexpr int WAVE_FLOATS = FM * FN * 16 * 64;  // one wave's accumulators
+    // Partial sums of group q (1..KG-1) go to block q-1 of the stage arrays
+    // As0, Bs0, As1, Bs1, ... (RED_PER_ARRAY blocks of BM*BN floats each).
+    auto red_block = [&](int q) -> float* {
+      const int a = (q - 1) / Cfg::RED_PER_ARRAY, off = ((q - 1) % Cfg::RED_PER_ARRAY) * BM * BN;
+      float* base = a == 0 ? As0 : a == 1 ? Bs0 : a == 2 ? As1 : a == 3 ? Bs1 : a == 4 ? As2 : Bs2;
+      return base + off + wt * WAVE_FLOATS + lane;
+    };
+    // The K loop ends with a barrier, so no wave still reads a slab.
+    if (kg > 0) {
+      float* red = red_block(kg);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+#pragma unroll
+    for (int q = 1; q < Cfg::KG; ++q) {
+      const float* red = red_block(q);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * FN + j) * 16 + r) * 64];
+    }
+  }
+
+  // ---- epilogue: masked stores; C is read only when beta != 0 ------------
+  float* C = g.C + (int64_t)blockIdx.y * g.strideC;
+  const int row0 = m0 + wm * Cfg::WTM + 4 * h;
+  const int col0 = n0 + wn * Cfg::WTN + l32;
+  const float alpha = g.alpha, beta = g.beta;
+  auto store_tile = [&](auto op) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = col0 + 32 * j;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + 32 * i + 8 * (r >> 2) + (r & 3);
+          if (row < M && col < N) op(C + (int64_t)row * g.ldc + col, acc[i][j][r]);
+        }
+      }
+  };
+  if (alpha == 1.0f && beta == 0.0f)
+    store_tile([](float* p, float v) { *p = v; });
+  else if (beta == 0.0f)
+    store_tile([alpha](float* p, float v) { *p = alpha * v; });
+  else
+    store_tile([alpha, beta](float* p, float v) { *p = __builtin_fmaf(beta, *p, alpha * v); });
+}
+
 // The LDS stage arrays of a kernel. Each stage is its own __shared__ array,
 // and code picks one with a compile-time index: the compiler then sees that a
 // direct load into one stage does not alias reads of another, and does not
@@ -220,14 +455,14 @@ struct Stages {
   __shared__ __attribute__((aligned(1024))) float Bs2[Cfg::STAGES > 2 ? Cfg::SlabB::FLOATS : 4]; \
   const Stages st{{As0, As1, As2}, {Bs0, Bs1, Bs2}}
 
-// DIRECT: every slab by direct loads (the launcher guarantees 16-byte aligned
-// chunks inside the matrices and K a multiple of BK); otherwise every slab
-// through registers. Two kernels rather than a branch, so each gets the
-// registers it needs. The direct kernels are held to the registers of
-// WAVES_EU waves per SIMD (128 VGPRs for four), so small tiles keep several
-// workgroups per compute unit instead of spending the register file on one.
+// tile_product: the per-tile K loop of mfma_dma_kernel above, as a function the
+// stream-K kernel calls once per piece of work (DIRECT and the register
+// budget as there). The plain kernel keeps its own copy of the loop: written
+// through this function it compiled to a slightly different K loop (one more
+// 64-bit address add per two slabs) that ran 0.75% slower at 8192^3 and
+// 4096^3, timed alternately against the original in one process.
 //
-// tile_product: the workgroup's BM x BN tile of op(A).op(B) at rows m0.., columns
+// It computes the workgroup's BM x BN tile of op(A).op(B) at rows m0.., columns
 // n0.., over k = 0 .. K-1 of the operands whose k = 0 lies at A and B. It hands
 // the accumulators to epi(acc, row0, col0) (with k groups, group 0 only, after the
 // groups' sums are added), where accumulator element r of block (i, j) belongs to
@@ -445,23 +680,6 @@ __device__ __forceinline__ void store_c(const f32x16 (&acc)[FM][FN], int row0, i
     store_tile([alpha](float* p, float v) { *p = alpha * v; });
   else
     store_tile([alpha, beta](float* p, float v) { *p = __builtin_fmaf(beta, *p, alpha * v); });
-}
-
-// One workgroup per tile of C (grid.x) and batch entry (grid.y).
-template <class Cfg, bool DIRECT>
-__global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_kernel(GemmArgs g) {
-  SGEMM_DMA_DECLARE_STAGES(Cfg, st);
-  const int K = (blockIdx.y == gridDim.y - 1) ? g.k_last : g.K;  // last split-K chunk may be short
-  const int tiles_m = (g.M + Cfg::BM - 1) / Cfg::BM, tiles_n = (g.N + Cfg::BN - 1) / Cfg::BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
-  const float* A = g.A + (int64_t)blockIdx.y * g.strideA;
-  const float* B = g.B + (int64_t)blockIdx.y * g.strideB;
-  float* C = g.C + (int64_t)blockIdx.y * g.strideC;
-  tile_product<Cfg, DIRECT>(g, st, A, B, K, tm * Cfg::BM, tn * Cfg::BN,
-                            [&](const f32x16(&acc)[Cfg::FM][Cfg::FN], int row0, int col0) {
-                              store_c(acc, row0, col0, C, g.ldc, g.M, g.N, g.alpha, g.beta);
-                            });
 }
 
 // Stream-K (Osama et al., "Stream-K: Work-centric Parallel Decomposition for
