@@ -68,6 +68,9 @@ def test_streamk_schedules_exact(cid):
         (3 * bm - 8, 2 * bn + 36, 70 * bk),  # 9 tiles, ranges cross tile boundaries
         (bm, bn, 3 * bk),                    # one tile in three pieces
         (2 * bm + 4, bn - 4, 33 * bk + 5),   # K tail: register staging
+        (1, bn + 4, 7),                      # one row, K shorter than a slab
+        (bm + 4, 1, 3 * bk),                 # one column
+        (64, 64, 300 * bk),                  # one tile in pieces on every workgroup of the grid
     ]
     for i, (M, N, K) in enumerate(cases):
         A, B = workloads.draw(M, N, K, 1000 + 10 * cid + i, "int4")
@@ -113,7 +116,7 @@ def test_streamk_alpha_beta_unaligned_exact(cid):
     G.check_exact(got, np_(A), np_(B))
 
 
-@pytest.mark.parametrize("cid", SK_IDS[:4], ids=[CONFIG_NAMES[i] for i in SK_IDS[:4]])
+@pytest.mark.parametrize("cid", SK_IDS, ids=[CONFIG_NAMES[i] for i in SK_IDS])
 def test_streamk_float_bound_and_repeatable(cid):
     bm, bn, bk, _ = sg.sgemm_mi355_config_info(cid)
     M, N, K = 5 * bm + 12, 4 * bn + 8, 512
