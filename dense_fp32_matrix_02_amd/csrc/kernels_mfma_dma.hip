@@ -23,9 +23,11 @@
 // Direct loads need 16-byte aligned global chunks that lie wholly inside the
 // matrices, and cannot zero k >= K. Lines past the edge of C are clamped to
 // the last line (or the last whole chunk of lines), which feeds only outputs
-// that are never stored; K must be a whole number of slabs. Problems that do
-// not allow this run a second instantiation that stages every slab through
-// registers instead (same layouts, edges and K tail zeroed in registers).
+// that are never stored. When K is not a whole number of slabs, a third
+// instantiation loads the whole slabs directly and stages only the last,
+// partial one through registers. Misaligned operands run an instantiation
+// that stages every slab through registers (same layouts, edges and K tail
+// zeroed in registers).
 
 #include <type_traits>
 
@@ -208,7 +210,10 @@ struct DmaCfg {
 // registers it needs. The direct kernels are held to the registers of
 // WAVES_EU waves per SIMD (128 VGPRs for four), so small tiles keep several
 // workgroups per compute unit instead of spending the register file on one.
-template <class Cfg, bool DIRECT>
+// KTAIL (with DIRECT, for K >= BK not a multiple of BK): the whole slabs by
+// direct loads, then the last, partial slab through registers with k >= K
+// zeroed, unpipelined, after the direct loop has freed the stage arrays.
+template <class Cfg, bool DIRECT, bool KTAIL = false>
 __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_kernel(GemmArgs g) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int ST = Cfg::STAGES, NW = Cfg::NW;
@@ -355,6 +360,15 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
     }
     if (s < nfull) step(S0{}, s);
     if (s + 1 < nfull) step(S1{}, s + 1);
+    if constexpr (KTAIL) {
+      if (tail) {
+        load_regs(nfull * BK, true);
+        store_regs(S0{});
+        __syncthreads();
+        compute(S0{});
+        if constexpr (Cfg::KG > 1) __syncthreads();  // the groups' sums reuse the stage arrays
+      }
+    }
   } else {
     // Register staging through stages 0 and 1, last slab peeled.
     const int nk = nfull + (tail ? 1 : 0);
@@ -461,6 +475,10 @@ struct Stages {
 // through this function it compiled to a slightly different K loop (one more
 // 64-bit address add per two slabs) that ran 0.75% slower at 8192^3 and
 // 4096^3, timed alternately against the original in one process.
+//
+// Unlike the plain kernel it has no direct variant with a register-staged last
+// slab: in the stream-K kernel that variant spilled 150 to 290 VGPRs, so a K
+// that is not a whole number of slabs takes the register-staged kernel here.
 //
 // It computes the workgroup's BM x BN tile of op(A).op(B) at rows m0.., columns
 // n0.., over k = 0 .. K-1 of the operands whose k = 0 lies at A and B. It hands
@@ -802,13 +820,26 @@ bool direct_ok(const GemmArgs& g) {
   return g.M > 0 && g.N > 0 && aligned && lines && g.K % Cfg::BK == 0 && g.k_last % Cfg::BK == 0;
 }
 
+// The direct kernel with a register-staged last slab: the same alignment, K
+// (and a short last split-K chunk) at least one slab but not all multiples of
+// BK. Its direct loads stop at the last whole slab of each batch entry.
+template <class Cfg>
+bool direct_tail_ok(const GemmArgs& g) {
+  const bool aligned = ((reinterpret_cast<uintptr_t>(g.A) | reinterpret_cast<uintptr_t>(g.B)) & 15) == 0 &&
+                       ((g.lda | g.ldb) & 3) == 0 && (g.batch <= 1 || ((g.strideA | g.strideB) & 3) == 0);
+  const bool lines = (Cfg::TA == 0 || g.M % 4 == 0) && (Cfg::TB != 0 || g.N % 4 == 0);
+  return g.M > 0 && g.N > 0 && aligned && lines && g.K >= Cfg::BK && g.k_last >= Cfg::BK &&
+         (g.K % Cfg::BK != 0 || g.k_last % Cfg::BK != 0);
+}
+
 template <class Cfg>
 hipError_t launch_mfma_dma(const GemmArgs& g, hipStream_t stream) {
   const int64_t tiles = (int64_t)((g.M + Cfg::BM - 1) / Cfg::BM) * ((g.N + Cfg::BN - 1) / Cfg::BN);
   GemmArgs a = g;
   void* args[] = {&a};
-  const void* kernel = direct_ok<Cfg>(g) ? reinterpret_cast<const void*>(&mfma_dma_kernel<Cfg, true>)
-                                         : reinterpret_cast<const void*>(&mfma_dma_kernel<Cfg, false>);
+  const void* kernel = direct_ok<Cfg>(g)        ? reinterpret_cast<const void*>(&mfma_dma_kernel<Cfg, true>)
+                       : direct_tail_ok<Cfg>(g) ? reinterpret_cast<const void*>(&mfma_dma_kernel<Cfg, true, true>)
+                                                : reinterpret_cast<const void*>(&mfma_dma_kernel<Cfg, false>);
   return hipLaunchKernel(kernel, dim3((unsigned)tiles, (unsigned)g.batch), dim3(Cfg::NT), args, 0, stream);
 }
 

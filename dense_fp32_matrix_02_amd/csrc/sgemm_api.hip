@@ -272,11 +272,18 @@ int rule_select(int opA, int opB, int M, int N, int K, int batch) {
 
 // Whether direct-to-LDS configuration c takes its direct path on this
 // problem (its launcher's condition, with `aligned` standing for the pointer,
-// leading-dimension and stride alignment): otherwise it stages through
-// registers, which its measured times do not describe.
+// leading-dimension and stride alignment): K of at least one slab (a last,
+// partial slab goes through registers at the end), and for a line-contiguous
+// operand an extent that is a multiple of 4. Otherwise it stages every slab
+// through registers, which its measured times do not describe.
 bool direct_path(const KernelConfig& c, int M, int N, int K, bool aligned) {
-  return aligned && M > 0 && N > 0 && K > 0 && K % c.bk == 0 && (!c.transA || M % 4 == 0) &&
-         (c.transB || N % 4 == 0);
+  return aligned && M > 0 && N > 0 && K >= c.bk && (!c.transA || M % 4 == 0) && (c.transB || N % 4 == 0);
+}
+
+// The stream-K kernels have no register-staged last slab: direct loads need K
+// to be a whole number of slabs there.
+bool streamk_direct(const KernelConfig& c, int M, int N, int K, bool aligned) {
+  return direct_path(c, M, N, K, aligned) && K % c.bk == 0;
 }
 
 // Model selection for a single product: the measured shape of this op pair
@@ -640,7 +647,7 @@ int run_streamk(const Problem& p, float* C, float* W, size_t w_bytes, hipStream_
     return SGEMM_MI355_ERR_CONFIG;
   if (p.M == 0 || p.N == 0) return SGEMM_MI355_OK;
   if (p.K == 0 || p.alpha == 0.0f) return run(p, C, stream, config);  // C = beta * C
-  const bool direct = direct_path(*cfg, p.M, p.N, p.K, operands_aligned(p));
+  const bool direct = streamk_direct(*cfg, p.M, p.N, p.K, operands_aligned(p));
   const int cus = device_compute_units(), occ = streamk_occupancy(*cfg, direct);
   if (cus <= 0 || occ <= 0) return SGEMM_MI355_ERR_LAUNCH;
   if (tiles_for(*cfg, p.M, p.N) > INT_MAX / 2) return SGEMM_MI355_ERR_EXTENT;
@@ -697,7 +704,7 @@ int select_streamk(int opA, int opB, int M, int N, int K, bool aligned) {
   for (size_t c = 0; c < rb.skid.size(); ++c) {
     const int id = rb.skid[c];
     const KernelConfig& cfg = *config_at(id);
-    if (!direct_path(cfg, M, N, K, aligned)) continue;
+    if (!streamk_direct(cfg, M, N, K, aligned)) continue;
     const int64_t tiles = tiles_for(cfg, M, N);
     if (tiles % ((int64_t)kCompute * rb.skocc[c]) == 0) continue;  // whole rounds: nothing to split
     const double slabs = (double)tiles * (double)(((int64_t)K + cfg.bk - 1) / cfg.bk) / kCompute;

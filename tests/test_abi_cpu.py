@@ -375,10 +375,12 @@ def _busy(cid, occ, M, N, K, batch=1):
 
 
 def _direct_path(name, M, N, K):
-    """A direct-to-LDS configuration takes its direct path (aligned operands)."""
+    """A direct-to-LDS configuration takes its direct path (aligned operands):
+    K of at least one slab (a partial last slab is staged through registers)
+    and a line-contiguous operand's extent a multiple of 4."""
     bk = sg.sgemm_mi355_config_info(_id(name))[2]
     opA, opB = sg.sgemm_mi355_config_ops(_id(name))
-    return M > 0 and N > 0 and K > 0 and K % bk == 0 and (not opA or M % 4 == 0) and (opB or N % 4 == 0)
+    return M > 0 and N > 0 and K >= bk and (not opA or M % 4 == 0) and (opB or N % 4 == 0)
 
 
 def _model_predict(blocks, opA, opB, M, N, K):
@@ -535,10 +537,11 @@ def _streamk_select(blocks, norms, sk, opA, opB, M, N, K):
     estimate is the larger of the nearest-shape prediction and the median
     model's for the configuration the plain path runs (the median model's
     own choice when no measured shape is near); each stream-K configuration
-    on its direct path whose tiles leave a partial last round of 256 x
-    occupancy workgroups is predicted as its time per slab x tiles x slabs /
-    256 + STREAMK_OVERHEAD_US; the least wins (first on a tie) if it is below
-    STREAMK_GAIN of the plain estimate. Returns a name or None."""
+    on its direct path with K a whole number of slabs, whose tiles leave a
+    partial last round of 256 x occupancy workgroups, is predicted as its
+    time per slab x tiles x slabs / 256 + STREAMK_OVERHEAD_US; the least wins
+    (first on a tie) if it is below STREAMK_GAIN of the plain estimate.
+    Returns a name or None."""
     import math
     plain = _model_predict(blocks, opA, opB, M, N, K)
     if plain is not None:
@@ -550,9 +553,9 @@ def _streamk_select(blocks, norms, sk, opA, opB, M, N, K):
         est, name = _global_predict(norms, opA, opB, M, N, K, 1)
     best = None
     for n, occ, us in sk.get((opA, opB), []):
-        if not _direct_path(n, M, N, K):
-            continue
         bm, bn, bk, _ = sg.sgemm_mi355_config_info(_id(n))
+        if not _direct_path(n, M, N, K) or K % bk:
+            continue  # the stream-K kernels take direct loads only for whole slabs
         tiles = math.ceil(M / bm) * math.ceil(N / bn)
         if tiles % (256 * occ) == 0:
             continue

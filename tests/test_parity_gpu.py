@@ -264,12 +264,13 @@ DIRECT_IDS = [i for i, n in enumerate(CONFIG_NAMES) if "_lds" in n]
 @pytest.mark.parametrize("cid", DIRECT_IDS, ids=[CONFIG_NAMES[i] for i in DIRECT_IDS])
 def test_direct_lds_configs_exact(cid):
     """Configurations that stage slabs with direct global-to-LDS loads take
-    that path only for 16-byte aligned operands, K a multiple of the slab
-    depth and, for a line-contiguous operand (B, or A^T), its extent a
-    multiple of 4; lines past the edge of C are clamped. Exercise it with
-    ragged M and N (multiples of 4 and not), slab counts that leave every
-    remainder of the stage count, then a batch and a split-K chunking, all
-    exact on integer inputs, in the operand layouts the configuration reads."""
+    that path only for 16-byte aligned operands, K of at least one slab (a
+    partial last slab is staged through registers) and, for a line-contiguous
+    operand (B, or A^T), its extent a multiple of 4; lines past the edge of C
+    are clamped. Exercise it with ragged M and N (multiples of 4 and not),
+    slab counts that leave every remainder of the stage count, a partial last
+    slab, then a batch and split-K chunkings, all exact on integer inputs, in
+    the operand layouts the configuration reads."""
     bm, bn, bk, _ = sg.sgemm_mi355_config_info(cid)
     opA, opB = sg.sgemm_mi355_config_ops(cid)
     seed = 500
@@ -296,6 +297,22 @@ def test_direct_lds_configs_exact(cid):
     M, N, K = bm - 8, bn, 70 * bk
     A, B = workloads.draw(M, N, K, 900, "int4")
     print(f"[gpu] config={CONFIG_NAMES[cid]} split-K M={M} N={N} K={K}", flush=True)
+    Cs = sg.gemm_splitk(G.dev(_stored(A, opA)), G.dev(_stored(B, opB)), splits=3, opA=opA, opB=opB, config=cid)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(Cs.cpu().numpy(), oracle.sgemm_f32(np_(A), np_(B)))
+    # K not a whole number of slabs (rows still 16-byte aligned): direct loads
+    # for the whole slabs, the last one staged through registers; K of one
+    # slab and a bit, every stage remainder, and a split-K whose chunks all end
+    # in a partial slab
+    for slabs in (1, 2, 3, 7):
+        for r in (4, bk - 4):
+            seed += 1
+            M, N, K = bm + 4, bn - 4, slabs * bk + r
+            A, B = workloads.draw(M, N, K, seed, "int4")
+            G.check_exact(_run_config(A, B, cid), np_(A), np_(B))
+    M, N, K = bm - 8, bn + 12, 70 * bk + 4
+    A, B = workloads.draw(M, N, K, 950, "int4")
+    print(f"[gpu] config={CONFIG_NAMES[cid]} split-K, partial slabs M={M} N={N} K={K}", flush=True)
     Cs = sg.gemm_splitk(G.dev(_stored(A, opA)), G.dev(_stored(B, opB)), splits=3, opA=opA, opB=opB, config=cid)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(Cs.cpu().numpy(), oracle.sgemm_f32(np_(A), np_(B)))
