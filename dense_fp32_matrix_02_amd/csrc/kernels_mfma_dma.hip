@@ -477,8 +477,8 @@ struct Stages {
 // 4096^3, timed alternately against the original in one process.
 //
 // Unlike the plain kernel it has no direct variant with a register-staged last
-// slab: in the stream-K kernel that variant spilled 150 to 290 VGPRs, so a K
-// that is not a whole number of slabs takes the register-staged kernel here.
+// slab: in the stream-K kernel that variant spilled 150 to 290 VGPRs. The
+// stream-K kernel adds a partial last slab in its epilogue instead.
 //
 // It computes the workgroup's BM x BN tile of op(A).op(B) at rows m0.., columns
 // n0.., over k = 0 .. K-1 of the operands whose k = 0 lies at A and B. It hands
@@ -700,6 +700,43 @@ __device__ __forceinline__ void store_c(const f32x16 (&acc)[FM][FN], int row0, i
     store_tile([alpha, beta](float* p, float v) { *p = __builtin_fmaf(beta, *p, alpha * v); });
 }
 
+// acc += the products of k = kt .. K-1 (fewer than a slab) for one wave's
+// accumulators, with rows and columns as tile_product hands them over: plain
+// FMAs on operand elements read straight from memory, zero for rows past M
+// and columns past N. The stream-K kernel adds a partial last slab this way
+// in the epilogue, since staging it through registers there spilled.
+template <class Cfg>
+__device__ __forceinline__ void add_k_tail(f32x16 (&acc)[Cfg::FM][Cfg::FN], const GemmArgs& g, int kt, int row0,
+                                           int col0) {
+  constexpr int T = Cfg::BK - 1;  // at most this many k values remain
+  // op(B) values of the tail for this lane's columns, then each row in turn
+  // with k innermost, so no per-row address stays live across rows
+  float bv[T][Cfg::FN];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int k = kt + t, col = col0 + 32 * j;
+      bv[t][j] = (k < g.K && col < g.N) ? (Cfg::TB ? g.B[(int64_t)col * g.ldb + k] : g.B[(int64_t)k * g.ldb + col])
+                                        : 0.0f;
+    }
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = row0 + 32 * i + 8 * (r >> 2) + (r & 3);
+      if (row >= g.M) continue;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int k = kt + t;
+        if (k >= g.K) break;
+        const float av = Cfg::TA ? g.A[(int64_t)k * g.lda + row] : g.A[(int64_t)row * g.lda + k];
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) acc[i][j][r] = __builtin_fmaf(av, bv[t][j], acc[i][j][r]);
+      }
+    }
+}
+
 // Stream-K (Osama et al., "Stream-K: Work-centric Parallel Decomposition for
 // Dense Matrix-Matrix Multiplication on the GPU", PPoPP 2023): a persistent
 // grid of G workgroups, about one per resident slot of the device. The first
@@ -714,7 +751,10 @@ __device__ __forceinline__ void store_c(const f32x16 (&acc)[FM][FN], int row0, i
 // (StreamKPlan). A second kernel then adds each split tile's partials in
 // ascending k order. Every workgroup's loop ends after its own range, so the
 // grid drains whether or not all of it is resident at once.
-template <class Cfg, bool DIRECT>
+// KTAIL (direct loads, K not a whole number of slabs): the iters slabs are
+// the whole ones, and the piece that ends a tile adds the k >= iters * BK
+// products in its epilogue (add_k_tail).
+template <class Cfg, bool DIRECT, bool KTAIL = false>
 __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1)
     mfma_dma_streamk_kernel(GemmArgs g, StreamKPlan p) {
   static_assert(Cfg::KG == 1, "stream-K runs tiles without k groups");
@@ -750,7 +790,10 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1)
     const int m0 = tm * BM, n0 = tn * BN;
     tile_product<Cfg, DIRECT>(
         g, st, g.A + SA::k_offset(k0, g.lda), g.B + SB::k_offset(k0, g.ldb), klen, m0, n0,
-        [&](const f32x16(&acc)[Cfg::FM][Cfg::FN], int row0, int col0) {
+        [&](f32x16(&acc)[Cfg::FM][Cfg::FN], int row0, int col0) {
+          if constexpr (KTAIL) {
+            if (ke == p.iters) add_k_tail<Cfg>(acc, g, p.iters * BK, row0, col0);
+          }
           if (whole) {
             store_c(acc, row0, col0, g.C, g.ldc, g.M, g.N, g.alpha, g.beta);
           } else {
@@ -847,13 +890,18 @@ template <class Cfg>
 hipError_t launch_mfma_dma_streamk(const GemmArgs& g, const StreamKPlan& plan, int grid, bool direct,
                                    hipStream_t stream) {
   // the direct kernel only where its loads stay aligned and inside the matrices
-  if (direct && !direct_ok<Cfg>(g)) return hipErrorInvalidValue;
+  // with direct loads a K that is not a whole number of slabs takes the KTAIL
+  // kernel, whose plan counts only the whole slabs
+  const bool ktail = direct && g.K % Cfg::BK != 0;
+  if (direct && !direct_ok<Cfg>(g) && !direct_tail_ok<Cfg>(g)) return hipErrorInvalidValue;
+  if (plan.iters != (ktail ? g.K / Cfg::BK : (g.K + Cfg::BK - 1) / Cfg::BK)) return hipErrorInvalidValue;
   if (grid <= 0 || plan.iters <= 0 || (plan.sk_tiles > 0 && plan.partials == nullptr)) return hipErrorInvalidValue;
   GemmArgs a = g;
   StreamKPlan pl = plan;
   void* args[] = {&a, &pl};
-  const void* kernel = direct ? reinterpret_cast<const void*>(&mfma_dma_streamk_kernel<Cfg, true>)
-                              : reinterpret_cast<const void*>(&mfma_dma_streamk_kernel<Cfg, false>);
+  const void* kernel = !direct ? reinterpret_cast<const void*>(&mfma_dma_streamk_kernel<Cfg, false>)
+                       : ktail ? reinterpret_cast<const void*>(&mfma_dma_streamk_kernel<Cfg, true, true>)
+                               : reinterpret_cast<const void*>(&mfma_dma_streamk_kernel<Cfg, true>);
   hipError_t err = hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(Cfg::NT), args, 0, stream);
   if (err != hipSuccess || plan.sk_tiles == 0) return err;
   int bm = Cfg::BM, bn = Cfg::BN, gr = grid;

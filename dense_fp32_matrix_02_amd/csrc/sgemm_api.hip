@@ -280,11 +280,6 @@ bool direct_path(const KernelConfig& c, int M, int N, int K, bool aligned) {
   return aligned && M > 0 && N > 0 && K >= c.bk && (!c.transA || M % 4 == 0) && (c.transB || N % 4 == 0);
 }
 
-// The stream-K kernels have no register-staged last slab: direct loads need K
-// to be a whole number of slabs there.
-bool streamk_direct(const KernelConfig& c, int M, int N, int K, bool aligned) {
-  return direct_path(c, M, N, K, aligned) && K % c.bk == 0;
-}
 
 // Model selection for a single product: the measured shape of this op pair
 // nearest (M, N, K) in (log M, log N, log K), among those within a factor of
@@ -600,10 +595,13 @@ int streamk_occupancy(const KernelConfig& c, bool direct) {
   return n;
 }
 
-StreamKPlan streamk_plan(const KernelConfig& c, int M, int N, int K, int grid) {
+// With direct loads and K not a whole number of slabs (ktail), the slabs dealt
+// out are the whole ones; the kernel adds the rest of K in each tile's last
+// piece.
+StreamKPlan streamk_plan(const KernelConfig& c, int M, int N, int K, int grid, bool ktail) {
   const int64_t tiles = tiles_for(c, M, N);
   const int64_t dp = tiles / grid * grid;
-  const int iters = (int)(((int64_t)K + c.bk - 1) / c.bk);
+  const int iters = ktail ? K / c.bk : (int)(((int64_t)K + c.bk - 1) / c.bk);
   return StreamKPlan{(int)dp, (int)(tiles - dp), iters, (tiles - dp) * iters, nullptr};
 }
 
@@ -618,7 +616,9 @@ uint64_t streamk_need(const KernelConfig& c, int M, int N, int K) {
     const int occ = streamk_occupancy(c, d != 0);
     if (occ <= 0) continue;
     const int grid = cus * occ;
-    if (streamk_plan(c, M, N, K, grid).sk_tiles > 0 && streamk_bytes(c, grid) > need) need = streamk_bytes(c, grid);
+    const bool ktail = d != 0 && K >= c.bk && K % c.bk != 0;
+    if (streamk_plan(c, M, N, K, grid, ktail).sk_tiles > 0 && streamk_bytes(c, grid) > need)
+      need = streamk_bytes(c, grid);
   }
   return need;
 }
@@ -647,12 +647,12 @@ int run_streamk(const Problem& p, float* C, float* W, size_t w_bytes, hipStream_
     return SGEMM_MI355_ERR_CONFIG;
   if (p.M == 0 || p.N == 0) return SGEMM_MI355_OK;
   if (p.K == 0 || p.alpha == 0.0f) return run(p, C, stream, config);  // C = beta * C
-  const bool direct = streamk_direct(*cfg, p.M, p.N, p.K, operands_aligned(p));
+  const bool direct = direct_path(*cfg, p.M, p.N, p.K, operands_aligned(p));
   const int cus = device_compute_units(), occ = streamk_occupancy(*cfg, direct);
   if (cus <= 0 || occ <= 0) return SGEMM_MI355_ERR_LAUNCH;
   if (tiles_for(*cfg, p.M, p.N) > INT_MAX / 2) return SGEMM_MI355_ERR_EXTENT;
   const int grid = cus * occ;
-  StreamKPlan plan = streamk_plan(*cfg, p.M, p.N, p.K, grid);
+  StreamKPlan plan = streamk_plan(*cfg, p.M, p.N, p.K, grid, direct && p.K % cfg->bk != 0);
   if (plan.sk_tiles == 0) return run(p, C, stream, config);  // whole rounds only: the plain launch
   const uint64_t need = streamk_bytes(*cfg, grid);
   if (W == nullptr) return SGEMM_MI355_ERR_NULL;
@@ -704,7 +704,7 @@ int select_streamk(int opA, int opB, int M, int N, int K, bool aligned) {
   for (size_t c = 0; c < rb.skid.size(); ++c) {
     const int id = rb.skid[c];
     const KernelConfig& cfg = *config_at(id);
-    if (!streamk_direct(cfg, M, N, K, aligned)) continue;
+    if (!direct_path(cfg, M, N, K, aligned)) continue;
     const int64_t tiles = tiles_for(cfg, M, N);
     if (tiles % ((int64_t)kCompute * rb.skocc[c]) == 0) continue;  // whole rounds: nothing to split
     const double slabs = (double)tiles * (double)(((int64_t)K + cfg.bk - 1) / cfg.bk) / kCompute;

@@ -537,8 +537,8 @@ def _streamk_select(blocks, norms, sk, opA, opB, M, N, K):
     estimate is the larger of the nearest-shape prediction and the median
     model's for the configuration the plain path runs (the median model's
     own choice when no measured shape is near); each stream-K configuration
-    on its direct path with K a whole number of slabs, whose tiles leave a
-    partial last round of 256 x occupancy workgroups, is predicted as its
+    on its direct path whose tiles leave a partial last round of 256 x
+    occupancy workgroups is predicted as its
     time per slab x tiles x slabs / 256 + STREAMK_OVERHEAD_US; the least wins
     (first on a tie) if it is below STREAMK_GAIN of the plain estimate.
     Returns a name or None."""
@@ -554,8 +554,8 @@ def _streamk_select(blocks, norms, sk, opA, opB, M, N, K):
     best = None
     for n, occ, us in sk.get((opA, opB), []):
         bm, bn, bk, _ = sg.sgemm_mi355_config_info(_id(n))
-        if not _direct_path(n, M, N, K) or K % bk:
-            continue  # the stream-K kernels take direct loads only for whole slabs
+        if not _direct_path(n, M, N, K):
+            continue
         tiles = math.ceil(M / bm) * math.ceil(N / bn)
         if tiles % (256 * occ) == 0:
             continue

@@ -4,8 +4,9 @@ Every configuration with a stream-K form runs, in the operand layouts it
 reads, on problems that cover the schedule's cases: tiles fewer than
 the slabs the grid can take (most workgroups get nothing), tiles fewer than
 the grid with ranges that cross tile boundaries, whole rounds of tiles
-followed by a partial round, a K tail and unaligned rows (the register-staged
-kernel), and alpha/beta. Integer inputs in {-4..4} are exact in any summation
+followed by a partial round, a partial last slab on aligned rows (added in the
+epilogue of each tile's last piece), a K tail and unaligned rows (the
+register-staged kernel), and alpha/beta. Integer inputs in {-4..4} are exact in any summation
 order, so the result must equal the oracle bit for bit; uniform inputs are
 held to the standard bound and must repeat bit for bit (the partial sums are
 added in a fixed order).
@@ -71,6 +72,9 @@ def test_streamk_schedules_exact(cid):
         (1, bn + 4, 7),                      # one row, K shorter than a slab
         (bm + 4, 1, 3 * bk),                 # one column
         (64, 64, 300 * bk),                  # one tile in pieces on every workgroup of the grid
+        (bm + 4, bn + 4, 5 * bk + 4),        # aligned rows, partial last slab: added in the epilogue
+        (3 * bm - 8, 2 * bn + 36, 70 * bk + 12),
+        (64, 64, 300 * bk + 8),
     ]
     for i, (M, N, K) in enumerate(cases):
         A, B = workloads.draw(M, N, K, 1000 + 10 * cid + i, "int4")
@@ -90,7 +94,7 @@ def test_streamk_rounds_then_split_exact(cid):
     while (-(-side * 256 // bm)) * (-(-side * 256 // bn)) <= 4 * cus:
         side += 1
     M, N = side * 256 + 4, side * 256 - 4
-    for K, seed in ((4 * bk, 31), (4 * bk + 3, 32)):  # direct loads; K tail
+    for K, seed in ((4 * bk, 31), (4 * bk + 3, 32), (4 * bk + 4, 33)):  # direct; registers; direct + tail
         A, B = workloads.draw(M, N, K, 2000 + seed + cid, "int4")
         C = _streamk(A, B, cid)
         An, Bn = np_(A), np_(B)
