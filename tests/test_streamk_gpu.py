@@ -1,15 +1,15 @@
 """GPU parity of the stream-K form (sgemm_mi355_streamk*) against the CPU oracle.
 
 Every configuration with a stream-K form runs, in the operand layouts it
-reads, on problems that cover the schedule's cases: tiles fewer than
-the slabs the grid can take (most workgroups get nothing), tiles fewer than
-the grid with ranges that cross tile boundaries, whole rounds of tiles
-followed by a partial round, a partial last slab on aligned rows (added in the
+reads, on problems that cover the schedule's cases: tiles fewer than the
+slabs the grid can take (most workgroups get nothing), tiles fewer than the
+grid with ranges that cross tile boundaries, whole rounds of tiles followed
+by a partial round, a partial last slab on aligned rows (added in the
 epilogue of each tile's last piece), a K tail and unaligned rows (the
-register-staged kernel), and alpha/beta. Integer inputs in {-4..4} are exact in any summation
-order, so the result must equal the oracle bit for bit; uniform inputs are
-held to the standard bound and must repeat bit for bit (the partial sums are
-added in a fixed order).
+register-staged kernel), and alpha/beta. Integer inputs in {-4..4} are exact
+in any summation order, so the result must equal the oracle bit for bit;
+uniform inputs are held to the standard bound and must repeat bit for bit
+(the partial sums are added in a fixed order).
 """
 from __future__ import annotations
 
