@@ -310,6 +310,17 @@ def test_direct_lds_configs_exact(cid):
             M, N, K = bm + 4, bn - 4, slabs * bk + r
             A, B = workloads.draw(M, N, K, seed, "int4")
             G.check_exact(_run_config(A, B, cid), np_(A), np_(B))
+    batch, M, N, K = 3, bm + 4, bn + 12, 9 * bk + 8  # a batch whose entries end in a partial slab
+    A = torch.stack([_stored(workloads.draw(M, N, K, 960 + b, "int4")[0], opA) for b in range(batch)])
+    B = torch.stack([_stored(workloads.draw(M, N, K, 970 + b, "int4")[1], opB) for b in range(batch)])
+    print(f"[gpu] config={CONFIG_NAMES[cid]} batch={batch} M={M} N={N} K={K}", flush=True)
+    C = sg.gemm_strided_batched(G.dev(A), G.dev(B), opA=opA, opB=opB, config=cid)
+    torch.cuda.synchronize()
+    for b in range(batch):
+        Ab = np_(A[b]).T if opA else np_(A[b])
+        Bb = np_(B[b]).T if opB else np_(B[b])
+        np.testing.assert_array_equal(C[b].cpu().numpy(),
+                                      oracle.sgemm_f32(np.ascontiguousarray(Ab), np.ascontiguousarray(Bb)))
     M, N, K = bm - 8, bn + 12, 70 * bk + 4
     A, B = workloads.draw(M, N, K, 950, "int4")
     print(f"[gpu] config={CONFIG_NAMES[cid]} split-K, partial slabs M={M} N={N} K={K}", flush=True)
