@@ -185,3 +185,27 @@ def test_streamk_errors_and_whole_rounds():
         assert rc == sg.OK
         torch.cuda.synchronize()
         G.check_exact_checksums(C.cpu().numpy(), np_(A), np_(B))
+
+
+@pytest.mark.parametrize("cid", SK_IDS, ids=[CONFIG_NAMES[i] for i in SK_IDS])
+def test_streamk_random_shapes_exact(cid):
+    """Seeded random shapes (M, N from 1 to 1500, K from 1 to 3000, K a
+    multiple of 4 or not, rows padded or not, alpha/beta or not): every
+    element exact against the oracle on integer inputs."""
+    import random
+    rng = random.Random(7000 + cid)
+    opA, opB = sg.sgemm_mi355_config_ops(cid)
+    for case in range(6):
+        M, N = rng.randint(1, 1500), rng.randint(1, 1500)
+        K = rng.choice([rng.randint(1, 3000), 4 * rng.randint(1, 750)])
+        pad = rng.random() < 0.3
+        A, B = workloads.draw(M, N, K, 9000 + 37 * cid + case, "int4")
+        lda = ((M if opA else K) + rng.randint(1, 5)) if pad else None
+        ldb = ((K if opB else N) + rng.randint(1, 5)) if pad else None
+        if rng.random() < 0.3:
+            C0 = workloads.draw(M, 1, N, 9500 + case, "int4")[0]
+            want = np_(C0).copy()
+            oracle.sgemm_ex_f32(0, 0, -2.0, np_(A), np_(B), 3.0, want)
+            np.testing.assert_array_equal(_streamk(A, B, cid, C=C0, alpha=-2.0, beta=3.0, lda=lda, ldb=ldb), want)
+        else:
+            G.check_exact(_streamk(A, B, cid, lda=lda, ldb=ldb), np_(A), np_(B))
