@@ -291,7 +291,8 @@ def config_geometry(name):
 def streamk_norms(rows, occ):
     """{name: (occupancy, microseconds per slab)} for the stream-K forms timed
     in `rows`: per configuration, the median over shapes where its direct
-    kernel splits tiles of (time - STREAMK_OVERHEAD_US) / (tiles * slabs / 256)."""
+    kernel splits tiles of (time - STREAMK_OVERHEAD_US) / (tiles * slabs / 256),
+    slabs counting a partial last one."""
     import dense_fp32_matrix_02_amd as sg
 
     known = set(sg.config_names())
@@ -304,7 +305,9 @@ def streamk_norms(rows, occ):
             cid = sg.config_id(n)
             bm, bn, bk, _ = sg.sgemm_mi355_config_info(cid)
             opA, opB = sg.sgemm_mi355_config_ops(cid)
-            if K % bk or (opA and M % 4) or (not opB and N % 4):
+            # the tuner's operands are contiguous, so a leading dimension is a row length
+            direct = K >= bk and (M % 4 == 0 if opA else K % 4 == 0) and (K % 4 == 0 if opB else N % 4 == 0)
+            if not direct:
                 continue  # register-staged kernel
             tiles = -(-M // bm) * -(-N // bn)
             if tiles % (256 * occ[n]) == 0:

@@ -610,3 +610,63 @@ def test_streamk_table_and_errors():
     # arguments that describe no product need no workspace
     assert sg.sgemm_mi355_streamk_workspace_size(0, 0, 0, 64, 64, -1) == 0
     assert sg.sgemm_mi355_streamk_workspace_size(3, 0, 64, 64, 64, -1) == 0
+
+
+def test_tuner_writes_the_table_it_documents(tmp_path):
+    """tune.write_table on synthetic measurements: the candidates are the
+    per-shape winners, times beyond TABLE_CUT x a shape's best are 0, every
+    configuration's median time per busy unit is recorded, the stream-K block
+    holds each configuration's median (time - overhead) per evenly dealt slab
+    over the shapes where its direct kernel splits tiles (register-staged
+    shapes and whole rounds left out), and the split-K block each shape's
+    fastest split count."""
+    import statistics
+    from dense_fp32_matrix_02_amd import tune
+    from tests._table import read_norms, read_split_table, read_streamk
+    big, mid, sk = "mfma32_256x256x16_w4x4_lds2", "mfma32_128x128x32_w2x2_kg2", "mfma32_128x256x16_w2x4_lds2"
+    occ = {big: 1, mid: 1, sk: 2}
+    rows = [
+        {"M": 8192, "N": 8192, "K": 8192, "ops": "nn", "batch": 1, "occupancy": occ,
+         "times_ms": {big: 7.5, mid: 8.5, sk: 16.0}},
+        {"M": 1024, "N": 1024, "K": 1024, "ops": "nn", "batch": 1, "occupancy": occ,
+         "times_ms": {big: 0.07, mid: 0.03, sk: 0.04}},
+        # stream-K grid rows: not plain shapes; one splits tiles, one is register-staged (K % 16),
+        # one fills whole rounds of 256x256 tiles
+        {"M": 5120, "N": 5120, "K": 5120, "ops": "nn", "batch": 1, "occupancy": occ, "streamk_grid": True,
+         "times_ms": {big: 2.2}, "streamk_ms": {big: 1.9, sk: 1.95}},
+        {"M": 2560, "N": 2560, "K": 8200, "ops": "nn", "batch": 1, "occupancy": occ, "streamk_grid": True,
+         "times_ms": {big: 1.0}, "streamk_ms": {big: 0.8, sk: 0.81}},
+        {"M": 2500, "N": 2500, "K": 8201, "ops": "nn", "batch": 1, "occupancy": occ, "streamk_grid": True,
+         "times_ms": {big: 1.0}, "streamk_ms": {big: 5.0, sk: 5.0}},
+        {"M": 4096, "N": 4096, "K": 4096, "ops": "nn", "batch": 1, "occupancy": occ, "streamk_grid": True,
+         "times_ms": {big: 0.96}, "streamk_ms": {big: 0.96, sk: 1.0}},
+        {"M": 64, "N": 64, "K": 4096, "ops": "nn", "batch": 1, "occupancy": occ,
+         "times_ms": {}, "splitk_ms": {"1": 0.4, "2": 0.2, "4": 0.1, "8": 0.15}},
+    ]
+    path = tmp_path / "table.inc"
+    tune.write_table(rows, str(path), reps=5)
+    blocks = _table(str(path))
+    cands, shapes, times = blocks[(0, 0)]
+    assert [n for n, _ in cands] == [big, mid]  # winners, in first-win order
+    assert shapes == [(8192, 8192, 8192), (1024, 1024, 1024)]  # stream-K grid rows left out
+    assert times[0] == [7500.0, 8500.0]
+    assert times[1] == [0.0, 30.0]  # 70 us > 2 x 30 us: cut
+    norms = {n: (o, us) for n, o, us in read_norms(str(path))[(0, 0)]}
+    for n in (big, mid, sk):
+        geo = tune.config_geometry(n)
+        want = statistics.median(r["times_ms"][n] * 1e3 / tune.busy_time(*geo, occ[n], r["M"], r["N"], r["K"])
+                                 for r in rows[:2] if n in r["times_ms"])
+        assert norms[n][0] == occ[n] and norms[n][1] == pytest.approx(want, rel=1e-4)
+    skn = {n: (o, us) for n, o, us in read_streamk(str(path))[(0, 0)]}
+    assert set(skn) == {big, sk}
+
+    def per_slab(ms, n, M, N, K):
+        bm, bn, bk, _ = sg.sgemm_mi355_config_info(_id(n))
+        return (ms * 1e3 - tune.STREAMK_OVERHEAD_US) / (-(-M // bm) * -(-N // bn) * -(-K // bk) / 256)
+    # 5120^3 and 2560^2 x 8200 count; 2500^2 x 8201 is register-staged, and 4096^3 fills whole
+    # rounds in both tiles (256 tiles of 256x256 on 256 workgroups, 512 of 128x256 on 512)
+    assert skn[big][1] == pytest.approx(statistics.median(
+        [per_slab(1.9, big, 5120, 5120, 5120), per_slab(0.8, big, 2560, 2560, 8200)]), rel=1e-4)
+    assert skn[sk] == (2, pytest.approx(statistics.median(
+        [per_slab(1.95, sk, 5120, 5120, 5120), per_slab(0.81, sk, 2560, 2560, 8200)]), rel=1e-4))
+    assert read_split_table(str(path)) == [(64, 64, 4096, 4)]
