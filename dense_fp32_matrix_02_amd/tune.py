@@ -46,8 +46,10 @@ TABLE_HEADER = """\
 // configuration runs.
 //
 // Per op pair: the candidates (configurations that are the fastest on at
-// least one measured shape) with their occupancy (workgroups one compute
-// unit holds, from the HIP runtime), then per shape {{M, N, K}} and the
+// least one measured shape, overall or among those without direct loads, so
+// that misaligned problems have register-staged candidates) with their
+// occupancy (workgroups one compute unit holds, from the HIP runtime), then
+// per shape {{M, N, K}} and the
 // candidates' median times in microseconds; 0 marks a time more than
 // {cut}x the shape's best (never a candidate there). Then every
 // configuration of the op pair with its occupancy and its median time per
@@ -319,8 +321,9 @@ def streamk_norms(rows, occ):
 
 def write_table(results, path, reps):
     """The tile table from single-product rows of any op pairs: per op pair,
-    the configurations that are fastest on at least one shape, their
-    occupancy, and each shape's times (0 beyond TABLE_CUT x its best).
+    the configurations that are fastest on at least one shape (overall, or
+    among those without direct loads), their occupancy, and each shape's
+    times (0 beyond TABLE_CUT x its best).
     Configurations the built library no longer has are left out."""
     import dense_fp32_matrix_02_amd as sg
 
@@ -339,8 +342,15 @@ def write_table(results, path, reps):
             occ = {}
             for r in rows:
                 occ.update(r.get("occupancy", {}))
+            # the fastest configuration of each shape, then the fastest of those
+            # without direct loads: direct-LDS configurations cannot serve
+            # problems off their direct path (misaligned operands), so the
+            # table also keeps the best register-staged one at every shape
             best = [min((n for n in r["times_ms"] if n.startswith("mfma")), key=r["times_ms"].get) for r in rows]
+            staged = [min((n for n in r["times_ms"] if n.startswith("mfma") and "_lds" not in n),
+                          key=r["times_ms"].get) for r in rows]
             cands = sorted(set(best), key=best.index)
+            cands += [n for n in sorted(set(staged), key=staged.index) if n not in cands]
             missing = [n for n in cands if n not in occ]
             if missing:
                 raise ValueError(f"no occupancy recorded for {missing} ({ops})")

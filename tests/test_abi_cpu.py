@@ -435,9 +435,12 @@ def test_tile_table_is_consistent():
             # the shape's best is stored, and nothing beyond 2x it (times have 5 significant digits)
             b = min(t for t in row if t > 0)
             assert all(t == 0 or t <= 2.0 * b * (1 + 1e-4) for t in row)
-        # every candidate is the fastest on at least one shape
+        # every candidate is the fastest on at least one shape, overall or among
+        # the configurations without direct loads
         winners = {cands[min((t, c) for c, t in enumerate(row) if t > 0)[1]][0] for row in times}
-        assert winners == {n for n, _ in cands}, pair
+        staged = {cands[min((t, c) for c, t in enumerate(row) if t > 0 and "_lds" not in cands[c][0])[1]][0]
+                  for row in times}
+        assert winners | staged == {n for n, _ in cands}, pair
 
 
 def test_model_selection_matches_its_definition():
