@@ -142,6 +142,26 @@ int main() {
     ref_sgemm_ex_f32(1, 1, M, N, K, 1.0f, A.data(), lda, B.data(), ldb, 0.0f, want.data(), ldc);
     check("direct-LDS tt configuration 300x260x160", rc, dC.get(), want);
   }
+  {  // K not a whole number of 16-deep slabs on aligned rows: the direct kernel with a
+     // register-staged last slab, forced by name, then the library's own choice
+    const int M = 300, N = 260, K = 164;
+    int cid = -1;
+    for (int i = 0; i < sgemm_mi355_num_configs(); ++i)
+      if (std::strcmp(sgemm_mi355_config_name(i), "mfma32_256x256x16_w4x4_lds2") == 0) cid = i;
+    Ints g(7);
+    std::vector<float> A = g.fill((size_t)M * K), B = g.fill((size_t)K * N);
+    std::vector<float> C0((size_t)M * N, nan), want = C0;
+    Dev dA(A), dB(B), dC(C0);
+    int rc = cid < 0 ? SGEMM_MI355_ERR_CONFIG
+                     : sgemm_mi355_with_config(M, N, K, dA.p, K, dB.p, N, dC.p, N, stream, cid);
+    HIP_OK(hipStreamSynchronize(stream));
+    ref_sgemm_f32(M, N, K, A.data(), K, B.data(), N, want.data(), N);
+    check("direct-LDS 256x256 with a partial last slab, 300x260x164", rc, dC.get(), want);
+    dC.put(C0);
+    rc = sgemm_mi355(M, N, K, dA.p, K, dB.p, N, dC.p, N, stream);
+    HIP_OK(hipStreamSynchronize(stream));
+    check("sgemm_mi355 300x260x164", rc, dC.get(), want);
+  }
   {  // strided batch with a shared B (strideB = 0)
     const int batch = 5, M = 70, N = 45, K = 33;
     Ints g(3);
