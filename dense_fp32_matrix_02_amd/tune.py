@@ -9,7 +9,7 @@ launches is recorded, with each configuration's occupancy (workgroups per
 compute unit, from the HIP runtime).
 
     python -m dense_fp32_matrix_02_amd.tune [--shapes 8192x8192x8192,...]
-        [--grid] [--reps 20] [--json results.json] [--table tile_table.inc]
+        [--grid | --smallk-grid] [--reps 20] [--json results.json] [--table tile_table.inc]
         [--ops nn|tn|nt|tt] [--batch B]
     python -m dense_fp32_matrix_02_amd.tune --from-json nn.json,tn.json,nt.json,tt.json \
         --table dense_fp32_matrix_02_amd/csrc/tile_table.inc
@@ -86,6 +86,16 @@ STREAMK_SHAPES = ((5120, 5120, 5120), (6144, 6144, 6144), (3072, 3072, 8192), (1
 # for every stream-K tile on 256 compute units), the fixup kernel and its launch.
 STREAMK_OVERHEAD_US = 40.0
 SPLIT_KS = (1024, 2048, 4096, 8192, 16384, 32768, 65536)
+# The side lengths of the plain grid and of the short-K grid, and the plain
+# grid's depths.
+GRID_SIDES = (128, 256, 512, 1024, 2048, 4096, 8192)
+GRID_KS = (256, 1024, 4096, 16384)
+# The short-K grid: products whose K is a few slabs, where the launch and the
+# store of C take much of the time. Their launches last microseconds, so they
+# are timed with more repetitions than the default.
+SMALLK_KS = (32, 96)
+SMALLK_REPS = 30
+SMALLK_WARMUP = 10
 
 
 def parse_shapes(text):
@@ -154,6 +164,9 @@ def main(argv=None):
     ap.add_argument("--shapes", default=",".join(f"{w.M}x{w.N}x{w.K}" for w in workloads.WORKLOADS))
     ap.add_argument("--grid", action="store_true",
                     help="also measure the grid M, N in {128..8192} (powers of two) x K in {256, 1024, 4096, 16384}")
+    ap.add_argument("--smallk-grid", action="store_true",
+                    help="measure the grid M, N in {128..8192} (powers of two) x K in {32, 96}, with at least "
+                         f"{SMALLK_REPS} repetitions and {SMALLK_WARMUP} warm-up launches (launches of a few microseconds)")
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kinds", default="mfma", help="mfma, valu or mfma,valu")
@@ -189,6 +202,12 @@ def main(argv=None):
         args.kinds = "none"
         args.splitk = "1,2,4,8,16,32,64"
         args.shapes = ",".join(f"{m}x{n}x{k}" for m in SPLIT_SIDES for n in SPLIT_SIDES for k in SPLIT_KS)
+    if args.smallk_grid:
+        if args.batch != 1 or args.grid:
+            ap.error("--smallk-grid times single products on its own grid")
+        args.reps = max(args.reps, SMALLK_REPS)
+        args.warmup = max(args.warmup, SMALLK_WARMUP)
+        args.shapes = ",".join(f"{m}x{n}x{k}" for m in GRID_SIDES for n in GRID_SIDES for k in SMALLK_KS)
     if args.streamk_grid:
         if args.batch != 1 or args.grid:
             ap.error("--streamk-grid times single products on its own grid")
@@ -210,9 +229,9 @@ def main(argv=None):
     shapes = parse_shapes(args.shapes)
     if args.grid:
         # Every M, N in [64, 16384] and K in [128, 32768] lies within a factor
-        # of two of a grid point in each dimension (the table's lookup radius).
-        sides = [128, 256, 512, 1024, 2048, 4096, 8192]
-        shapes += [(m, n, k) for m in sides for n in sides for k in (256, 1024, 4096, 16384)
+        # of two of a grid point in each dimension (the table's lookup radius);
+        # the short-K grid extends K down to 16.
+        shapes += [(m, n, k) for m in GRID_SIDES for n in GRID_SIDES for k in GRID_KS
                    if (m, n, k) not in shapes]
     # stream-K forms are timed whatever --kinds says
     sk_cands = [i for i in range(len(names)) if sg.sgemm_mi355_config_streamk(i) == 1
@@ -221,7 +240,7 @@ def main(argv=None):
     tag = ("" if args.ops == "nn" else f" {args.ops}") + ("" if args.batch == 1 else f" x{args.batch}")
     for (M, N, K) in shapes:
         Ad, Bd, C = make_inputs(M, N, K, opA, opB, args.batch)
-        row = {"M": M, "N": N, "K": K, "ops": args.ops, "batch": args.batch, "times_ms": {},
+        row = {"M": M, "N": N, "K": K, "ops": args.ops, "batch": args.batch, "reps": args.reps, "times_ms": {},
                "occupancy": occupancy, "streamk_grid": bool(args.streamk_grid)}
         flops = 2 * M * N * K * args.batch
         shape_cands = [sg.sgemm_mi355_select_config_ex(opA, opB, M, N, K, args.batch)] if args.selected else cands
@@ -330,7 +349,10 @@ def write_table(results, path, reps):
     known = set(sg.config_names())
     results = [dict(r, times_ms={n: t for n, t in r["times_ms"].items() if n in known}) for r in results]
     with open(path, "w") as f:
-        f.write(TABLE_HEADER.format(reps=reps, cut=TABLE_CUT))
+        # rows record the repetitions they were timed with; older ones take `reps`
+        counts = sorted({r.get("reps", reps) for r in results}) or [reps]
+        text = str(counts[0]) if len(counts) == 1 else f"{counts[0]} to {counts[-1]}"
+        f.write(TABLE_HEADER.format(reps=text, cut=TABLE_CUT))
         blocks = []
         for ops in OPS_NAMES:
             sk_rows = [r for r in results if r.get("ops", "nn") == ops and r.get("streamk_ms")]

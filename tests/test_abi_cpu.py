@@ -615,6 +615,17 @@ def test_streamk_table_and_errors():
     assert sg.sgemm_mi355_streamk_workspace_size(3, 0, 64, 64, 64, -1) == 0
 
 
+def test_tuner_grids_reach_every_depth():
+    """Every M, N in [64, 16384] and K in [16, 32768] is within a factor of
+    two of a shape of the plain or the short-K grid (the nearest-shape radius)."""
+    from dense_fp32_matrix_02_amd import tune
+    ks = tune.GRID_KS + tune.SMALLK_KS
+    near = lambda x, pts: any(x <= 2 * p and p <= 2 * x for p in pts)
+    assert all(near(k, ks) for k in range(16, 32769))
+    assert all(near(m, tune.GRID_SIDES) for m in range(64, 16385))
+    assert not near(15, ks) and not near(32769, ks)
+
+
 def test_tuner_writes_the_table_it_documents(tmp_path):
     """tune.write_table on synthetic measurements: the candidates are the
     per-shape winners, times beyond TABLE_CUT x a shape's best are 0, every
@@ -631,7 +642,7 @@ def test_tuner_writes_the_table_it_documents(tmp_path):
     rows = [
         {"M": 8192, "N": 8192, "K": 8192, "ops": "nn", "batch": 1, "occupancy": occ,
          "times_ms": {big: 7.5, mid: 8.5, sk: 16.0}},
-        {"M": 1024, "N": 1024, "K": 1024, "ops": "nn", "batch": 1, "occupancy": occ,
+        {"M": 1024, "N": 1024, "K": 1024, "ops": "nn", "batch": 1, "occupancy": occ, "reps": 30,
          "times_ms": {big: 0.07, mid: 0.03, sk: 0.04}},
         # stream-K grid rows: not plain shapes; one splits tiles, one is register-staged (K % 16),
         # one fills whole rounds of 256x256 tiles
@@ -648,6 +659,8 @@ def test_tuner_writes_the_table_it_documents(tmp_path):
     ]
     path = tmp_path / "table.inc"
     tune.write_table(rows, str(path), reps=5)
+    # rows without a recorded repetition count take the argument's
+    assert "median of 5 to 30 launches" in path.read_text()
     blocks = _table(str(path))
     cands, shapes, times = blocks[(0, 0)]
     assert [n for n, _ in cands] == [big, mid]  # winners, in first-win order
