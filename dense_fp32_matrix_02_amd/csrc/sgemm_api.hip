@@ -41,7 +41,8 @@ struct TableBlock {
   int nnorm;
   const TableNorm* norms;  // every configuration of the op pair
   // stream-K forms: microseconds per slab of the evenly dealt work (beyond
-  // kStreamKOverheadUs), median over the stream-K grid
+  // kStreamKOverheadUs, the store of C counted as kStoreDepth / BK slabs per
+  // tile), median over the stream-K grid
   int nstreamk;
   const TableNorm* streamk;
 };
@@ -179,10 +180,15 @@ bool is_direct_config(int id) { return id >= kNumMfmaConfigs && id < kNumMfmaCon
 // kSatChains independent 32x32 accumulator blocks are resident (two per
 // SIMD, so one block's matrix instructions, or its wave's loads, overlap
 // another's); with b < kSatChains resident, a workgroup takes kSatChains / b
-// times as long. A workgroup holds kgroups * (BM/32) * (BN/32) blocks. The
-// busy time, in units of one workgroup slab step at full rate, is
-//   n * max(1, kSatChains / (min(n, occ) * blocks per workgroup)) * ceil(K / BK).
+// times as long. A workgroup holds kgroups * (BM/32) * (BN/32) blocks. Its
+// store of C counts as kStoreDepth more steps of k: with every CU storing,
+// a CU's share of the 8 TB/s writes a BM x BN tile of 4-byte values in the
+// time its share of the 157.3 TFLOP/s peak spends on 2 * BM * BN * 39 flops.
+// The busy time, in units of one workgroup slab step at full rate, is
+//   n * max(1, kSatChains / (min(n, occ) * blocks per workgroup))
+//     * (ceil(K / BK) + kStoreDepth / BK).
 constexpr int kSatChains = 8;
+constexpr double kStoreDepth = 40.0;
 
 double busy_time(const KernelConfig& c, int occ, int M, int N, int K, int batch) {
   const int64_t wgs = tiles_for(c, M, N) * (int64_t)(batch < kMaxGridY ? batch : kMaxGridY);
@@ -191,7 +197,7 @@ double busy_time(const KernelConfig& c, int occ, int M, int N, int K, int batch)
   const int64_t blocks = (int64_t)(c.kgroups > 0 ? c.kgroups : 1) * (c.bm / 32) * (c.bn / 32);
   const int64_t resident = (n < occ ? n : occ) * blocks;
   const double stretch = resident >= kSatChains ? 1.0 : (double)kSatChains / (double)resident;
-  return (double)n * stretch * (double)(((int64_t)K + c.bk - 1) / c.bk);
+  return (double)n * stretch * ((double)(((int64_t)K + c.bk - 1) / c.bk) + kStoreDepth / c.bk);
 }
 
 const Resolved& resolved() {
@@ -668,7 +674,8 @@ int run_streamk(const Problem& p, float* C, float* W, size_t w_bytes, hipStream_
 // kernel would run (the register-staged stream-K kernels were slower than the
 // plain path on every shape measured) and that leaves a partial last round is
 // predicted as its measured time per slab (the table's stream-K block) times
-// tiles * slabs / kCompute, plus kStreamKOverheadUs: the partial sums, two
+// tiles * (slabs + kStoreDepth / BK) / kCompute (every tile's store of C
+// counted as in busy_time), plus kStreamKOverheadUs: the partial sums, two
 // BM x BN blocks per workgroup of the grid (occupancy x BM x BN is the same
 // for every stream-K tile, 128 MiB on 256 compute units), the fixup kernel
 // and its launch. The plain path's time is the larger of the nearest-shape
@@ -676,8 +683,14 @@ int run_streamk(const Problem& p, float* C, float* W, size_t w_bytes, hipStream_
 // a measured shape with a different fill, the first can be optimistic
 // (1280 x 1280 x 32768: 0.71 ms predicted, 1.13 ms measured). Stream-K is
 // chosen when it is predicted below kStreamKGain of that; otherwise -1.
+// The time per slab was measured with K from 2048 up; like the nearest-shape
+// lookup, the model is not carried beyond a factor of two of that, so K below
+// kStreamKMinK keeps the plain path (at two slabs per tile, 10000 x 10000 x 30
+// would take stream-K on a median estimate of 160 us where the plain path
+// runs in 109).
 constexpr double kStreamKOverheadUs = 40.0;
 constexpr double kStreamKGain = 0.97;
+constexpr int kStreamKMinK = 1024;
 
 // The median model's estimate for configuration `id` (0 if the table has none).
 double global_estimate(int opA, int opB, int id, int M, int N, int K) {
@@ -688,7 +701,7 @@ double global_estimate(int opA, int opB, int id, int M, int N, int K) {
 }
 
 int select_streamk(int opA, int opB, int M, int N, int K, bool aligned) {
-  if (M <= 0 || N <= 0 || K <= 0) return -1;
+  if (M <= 0 || N <= 0 || K < kStreamKMinK) return -1;
   double plain_us = 0.0;
   int plain = model_select(opA, opB, M, N, K, aligned, &plain_us);
   if (plain >= 0) {
@@ -707,7 +720,8 @@ int select_streamk(int opA, int opB, int M, int N, int K, bool aligned) {
     if (!direct_path(cfg, M, N, K, aligned)) continue;
     const int64_t tiles = tiles_for(cfg, M, N);
     if (tiles % ((int64_t)kCompute * rb.skocc[c]) == 0) continue;  // whole rounds: nothing to split
-    const double slabs = (double)tiles * (double)(((int64_t)K + cfg.bk - 1) / cfg.bk) / kCompute;
+    const double slabs =
+        (double)tiles * ((double)(((int64_t)K + cfg.bk - 1) / cfg.bk) + kStoreDepth / cfg.bk) / kCompute;
     const double t = rb.sknorm[c] * slabs + kStreamKOverheadUs;
     if (best < 0 || t < best_t) {
       best = id;
@@ -951,6 +965,6 @@ const char* sgemm_mi355_strerror(int code) {
   }
 }
 
-const char* sgemm_mi355_version(void) { return "0.6.0"; }
+const char* sgemm_mi355_version(void) { return "0.6.1"; }
 
 }  // extern "C"

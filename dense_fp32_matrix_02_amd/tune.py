@@ -85,6 +85,9 @@ STREAMK_SHAPES = ((5120, 5120, 5120), (6144, 6144, 6144), (3072, 3072, 8192), (1
 # sgemm_api.hip): the partial sums (two BM x BN blocks per workgroup, 128 MiB
 # for every stream-K tile on 256 compute units), the fixup kernel and its launch.
 STREAMK_OVERHEAD_US = 40.0
+# The selection considers stream-K only for K from half the grid's smallest K
+# (kStreamKMinK in sgemm_api.hip): the time per slab is not carried further.
+STREAMK_MIN_K = min(k for _, _, k in STREAMK_SHAPES) // 2
 SPLIT_KS = (1024, 2048, 4096, 8192, 16384, 32768, 65536)
 # The side lengths of the plain grid and of the short-K grid, and the plain
 # grid's depths.
@@ -286,8 +289,11 @@ def main(argv=None):
 
 # Fill model of the selection (busy_time in csrc/sgemm_api.hip): the busiest
 # compute unit's share of workgroups, stretched while fewer than SAT_CHAINS
-# 32x32 accumulator blocks are resident, times the slab count.
+# 32x32 accumulator blocks are resident, times the slab count plus the store
+# of C as STORE_DEPTH / BK more slabs (a CU's share of HBM bandwidth writes a
+# tile in the time its share of the peak spends on about 40 steps of k).
 SAT_CHAINS = 8
+STORE_DEPTH = 40.0
 
 
 def busy_time(bm, bn, bk, kgroups, occ, M, N, K, batch=1):
@@ -295,7 +301,7 @@ def busy_time(bm, bn, bk, kgroups, occ, M, N, K, batch=1):
     n = -(-wgs // 256)
     resident = min(n, occ) * kgroups * (bm // 32) * (bn // 32)
     stretch = 1.0 if resident >= SAT_CHAINS else SAT_CHAINS / resident
-    return n * stretch * -(-K // bk)
+    return n * stretch * (-(-K // bk) + STORE_DEPTH / bk)
 
 
 def config_geometry(name):
@@ -312,8 +318,9 @@ def config_geometry(name):
 def streamk_norms(rows, occ):
     """{name: (occupancy, microseconds per slab)} for the stream-K forms timed
     in `rows`: per configuration, the median over shapes where its direct
-    kernel splits tiles of (time - STREAMK_OVERHEAD_US) / (tiles * slabs / 256),
-    slabs counting a partial last one."""
+    kernel splits tiles of (time - STREAMK_OVERHEAD_US) / (tiles * (slabs +
+    STORE_DEPTH / BK) / 256), slabs counting a partial last one and the store
+    of each tile counted as in busy_time."""
     import dense_fp32_matrix_02_amd as sg
 
     known = set(sg.config_names())
@@ -333,7 +340,7 @@ def streamk_norms(rows, occ):
             tiles = -(-M // bm) * -(-N // bn)
             if tiles % (256 * occ[n]) == 0:
                 continue  # whole rounds: the plain launch ran
-            slabs = tiles * -(-K // bk) / 256
+            slabs = tiles * (-(-K // bk) + STORE_DEPTH / bk) / 256
             per.setdefault(n, []).append((ms * 1e3 - STREAMK_OVERHEAD_US) / slabs)
     return {n: (occ[n], statistics.median(v)) for n, v in sorted(per.items())}
 

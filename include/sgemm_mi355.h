@@ -350,7 +350,7 @@ int sgemm_mi355_tile_map(int bid, int tiles_m, int tiles_n, int group_m, int *tm
 /* Static message for an error code (never NULL). */
 const char *sgemm_mi355_strerror(int code);
 
-/* Library version string, e.g. "0.6.0". */
+/* Library version string, e.g. "0.6.1". */
 const char *sgemm_mi355_version(void);
 
 #ifdef __cplusplus

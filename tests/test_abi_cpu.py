@@ -347,6 +347,7 @@ def test_select_splitk_matches_its_definition():
 from tests._table import OP_PAIRS, read_table as _table  # noqa: E402
 
 SAT_CHAINS = 8         # resident 32x32 accumulator blocks per compute unit for full rate
+STORE_DEPTH = 40.0     # the store of a C tile, in steps of k at full rate
 
 
 _IDS = {}
@@ -362,7 +363,8 @@ def _busy(cid, occ, M, N, K, batch=1):
     """Busy time of the busiest compute unit: n = ceil(workgroups / 256)
     workgroups, run occ at a time, stretched by SAT_CHAINS / resident
     accumulator blocks while fewer are resident (a workgroup holds
-    k-groups * BM/32 * BN/32 blocks of 32x32), times ceil(K / BK)."""
+    k-groups * BM/32 * BN/32 blocks of 32x32), times ceil(K / BK) plus
+    STORE_DEPTH / BK for the store of C."""
     import math
     bm, bn, bk, _ = sg.sgemm_mi355_config_info(cid)
     kg = re.search(r"_kg(\d+)", sg.sgemm_mi355_config_name(cid))
@@ -371,7 +373,7 @@ def _busy(cid, occ, M, N, K, batch=1):
     n = math.ceil(wgs / 256)
     resident = min(n, occ) * blocks
     stretch = 1.0 if resident >= SAT_CHAINS else SAT_CHAINS / resident
-    return n * stretch * math.ceil(K / bk)
+    return n * stretch * (math.ceil(K / bk) + STORE_DEPTH / bk)
 
 
 def _direct_path(name, M, N, K):
@@ -541,11 +543,14 @@ def _streamk_select(blocks, norms, sk, opA, opB, M, N, K):
     model's for the configuration the plain path runs (the median model's
     own choice when no measured shape is near); each stream-K configuration
     on its direct path whose tiles leave a partial last round of 256 x
-    occupancy workgroups is predicted as its
-    time per slab x tiles x slabs / 256 + STREAMK_OVERHEAD_US; the least wins
+    occupancy workgroups is predicted as its time per slab x tiles x
+    (slabs + STORE_DEPTH / BK) / 256 + STREAMK_OVERHEAD_US; the least wins
     (first on a tie) if it is below STREAMK_GAIN of the plain estimate.
-    Returns a name or None."""
+    K below tune.STREAMK_MIN_K keeps the plain path. Returns a name or None."""
     import math
+    from dense_fp32_matrix_02_amd import tune
+    if K < tune.STREAMK_MIN_K:
+        return None
     plain = _model_predict(blocks, opA, opB, M, N, K)
     if plain is not None:
         est, name = plain
@@ -562,7 +567,7 @@ def _streamk_select(blocks, norms, sk, opA, opB, M, N, K):
         tiles = math.ceil(M / bm) * math.ceil(N / bn)
         if tiles % (256 * occ) == 0:
             continue
-        t = us * (tiles * math.ceil(K / bk) / 256) + STREAMK_OVERHEAD_US
+        t = us * (tiles * (math.ceil(K / bk) + STORE_DEPTH / bk) / 256) + STREAMK_OVERHEAD_US
         if best is None or t < best[0]:
             best = (t, n)
     return best[1] if best is not None and best[0] < STREAMK_GAIN * est else None
@@ -584,6 +589,9 @@ def test_streamk_selection_matches_its_definition():
                  (4096, 4096, 4096), (5120, 5120, 5121), (5122, 5120, 5120), (5120, 5122, 5120), (3001, 2047, 1537)]
         cases += [(4 * rng.randint(16, 4096), 4 * rng.randint(16, 4096), 16 * rng.randint(8, 4096)) for _ in range(120)]
         cases += [(rng.randint(64, 16384), rng.randint(64, 16384), rng.randint(128, 65536)) for _ in range(40)]
+        # short K, around the smallest K considered (1024)
+        cases += [(10000, 10000, 30), (12000, 4000, 40), (10240, 10240, 1023), (10240, 10240, 1024)]
+        cases += [(4 * rng.randint(512, 4096), 4 * rng.randint(512, 4096), 16 * rng.randint(1, 128)) for _ in range(40)]
         for M, N, K in cases:
             want = _streamk_select(blocks, norms, sk, opA, opB, M, N, K)
             got = sg.sgemm_mi355_select_streamk(opA, opB, M, N, K)
@@ -591,6 +599,7 @@ def test_streamk_selection_matches_its_definition():
             chosen += want is not None
             plain += want is None
         assert sg.sgemm_mi355_select_streamk(opA, opB, 8192, 8192, 8192) == -1  # whole rounds
+        assert sg.sgemm_mi355_select_streamk(opA, opB, 10000, 10000, 30) == -1  # short K
     assert chosen > 100 and plain > 100
 
 
@@ -678,7 +687,7 @@ def test_tuner_writes_the_table_it_documents(tmp_path):
 
     def per_slab(ms, n, M, N, K):
         bm, bn, bk, _ = sg.sgemm_mi355_config_info(_id(n))
-        return (ms * 1e3 - tune.STREAMK_OVERHEAD_US) / (-(-M // bm) * -(-N // bn) * -(-K // bk) / 256)
+        return (ms * 1e3 - tune.STREAMK_OVERHEAD_US) / (-(-M // bm) * -(-N // bn) * (-(-K // bk) + STORE_DEPTH / bk) / 256)
     # 5120^3 and 2560^2 x 8200 count; 2500^2 x 8201 is register-staged, and 4096^3 fills whole
     # rounds in both tiles (256 tiles of 256x256 on 256 workgroups, 512 of 128x256 on 512)
     assert skn[big][1] == pytest.approx(statistics.median(
