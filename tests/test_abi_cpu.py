@@ -651,7 +651,7 @@ def test_tuner_writes_the_table_it_documents(tmp_path):
     rows = [
         {"M": 8192, "N": 8192, "K": 8192, "ops": "nn", "batch": 1, "occupancy": occ,
          "times_ms": {big: 7.5, mid: 8.5, sk: 16.0}},
-        {"M": 1024, "N": 1024, "K": 1024, "ops": "nn", "batch": 1, "occupancy": occ, "reps": 30,
+        {"M": 1024, "N": 1024, "K": 1024, "ops": "nn", "batch": 1, "occupancy": occ, "reps": 30, "passes": 2,
          "times_ms": {big: 0.07, mid: 0.03, sk: 0.04}},
         # stream-K grid rows: not plain shapes; one splits tiles, one is register-staged (K % 16),
         # one fills whole rounds of 256x256 tiles
@@ -669,7 +669,7 @@ def test_tuner_writes_the_table_it_documents(tmp_path):
     path = tmp_path / "table.inc"
     tune.write_table(rows, str(path), reps=5)
     # rows without a recorded repetition count take the argument's
-    assert "median of 5 to 30 launches" in path.read_text()
+    assert "median of 5 to 30 launches per\n// configuration and shape, the least over up to 2 passes)" in path.read_text()
     blocks = _table(str(path))
     cands, shapes, times = blocks[(0, 0)]
     assert [n for n, _ in cands] == [big, mid]  # winners, in first-win order
