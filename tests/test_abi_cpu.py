@@ -635,6 +635,14 @@ def test_tuner_grids_reach_every_depth():
     assert not near(15, ks) and not near(32769, ks)
 
 
+@pytest.mark.parametrize("argv", [["--passes", "0"], ["--smallk-grid", "--grid"],
+                                  ["--smallk-grid", "--batch", "4"]])
+def test_tuner_rejects_bad_options_before_timing(argv):
+    from dense_fp32_matrix_02_amd import tune
+    with pytest.raises(SystemExit):
+        tune.main(argv)
+
+
 def test_tuner_writes_the_table_it_documents(tmp_path):
     """tune.write_table on synthetic measurements: the candidates are the
     per-shape winners, times beyond TABLE_CUT x a shape's best are 0, every
