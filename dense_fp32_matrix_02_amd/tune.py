@@ -104,6 +104,18 @@ SMALLK_WARMUP = 10
 SMALLK_PASSES = 2
 
 
+def time_passes(names, passes, timer):
+    """{name: least of `passes` timings}: each pass times every name in order
+    with timer(name), so a slow spell hits one configuration's passes only if
+    it lasts through the others' timings in between."""
+    best = {}
+    for _ in range(passes):
+        for name in names:
+            ms = timer(name)
+            best[name] = min(ms, best.get(name, ms))
+    return best
+
+
 def parse_shapes(text):
     out = []
     for s in text.split(","):
@@ -257,13 +269,10 @@ def main(argv=None):
                "occupancy": occupancy, "streamk_grid": bool(args.streamk_grid)}
         flops = 2 * M * N * K * args.batch
         shape_cands = [sg.sgemm_mi355_select_config_ex(opA, opB, M, N, K, args.batch)] if args.selected else cands
-        # with several passes, each over all of the shape's configurations,
-        # a configuration keeps its least median
-        for _ in range(args.passes):
-            for cid in shape_cands:
-                ms = time_call(config_call(Ad, Bd, C, cid, opA, opB, args.batch), args.reps, args.warmup)
-                ms = min(ms, row["times_ms"].get(names[cid], ms))
-                row["times_ms"][names[cid]] = ms
+        row["times_ms"].update(time_passes(
+            [names[cid] for cid in shape_cands], args.passes,
+            lambda name: time_call(config_call(Ad, Bd, C, sg.config_id(name), opA, opB, args.batch),
+                                   args.reps, args.warmup)))
         for cid in shape_cands:
             ms = row["times_ms"][names[cid]]
             print(f"{M}x{N}x{K}{tag} {names[cid]:28s} {ms:9.4f} ms {flops / ms / 1e9:9.2f} TFLOP/s",

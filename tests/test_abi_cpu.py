@@ -643,6 +643,22 @@ def test_tuner_rejects_bad_options_before_timing(argv):
         tune.main(argv)
 
 
+def test_tuner_passes_keep_each_configurations_least_time():
+    """time_passes times every configuration once per pass, passes in turn,
+    and keeps each one's least timing."""
+    from dense_fp32_matrix_02_amd import tune
+    calls = []
+    slow = {("a", 0): 14.0, ("a", 1): 7.0, ("b", 0): 8.0, ("b", 1): 9.0}
+
+    def timer(name):
+        n = sum(1 for c in calls if c == name)
+        calls.append(name)
+        return slow[(name, n)]
+    assert tune.time_passes(["a", "b"], 2, timer) == {"a": 7.0, "b": 8.0}
+    assert calls == ["a", "b", "a", "b"]
+    assert tune.time_passes(["a"], 1, lambda n: 3.0) == {"a": 3.0}
+
+
 def test_tuner_writes_the_table_it_documents(tmp_path):
     """tune.write_table on synthetic measurements: the candidates are the
     per-shape winners, times beyond TABLE_CUT x a shape's best are 0, every
