@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     sgemm_mi355_config_name, sgemm_mi355_config_occupancy, sgemm_mi355_config_ops, sgemm_mi355_ex,
     sgemm_mi355_num_configs,
     sgemm_mi355_select_config, sgemm_mi355_select_config_ex, sgemm_mi355_select_config_valu,
+    sgemm_mi355_selected_config, sgemm_mi355_config_staging,
     sgemm_mi355_select_splitk, sgemm_mi355_select_streamk, sgemm_mi355_config_streamk,
     sgemm_mi355_streamk, sgemm_mi355_streamk_with_config, sgemm_mi355_streamk_workspace_size,
     sgemm_mi355_splitk, sgemm_mi355_splitk_with_config, sgemm_mi355_splitk_workspace_size, sgemm_mi355_strerror,

@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sgemm_mi355_config_ops.argtypes = [_I, ctypes.POINTER(_I), ctypes.POINTER(_I)]
     lib.sgemm_mi355_config_occupancy.argtypes = [_I, ctypes.POINTER(_I)]
     lib.sgemm_mi355_select_config.argtypes = [_I, _I, _I]
+    lib.sgemm_mi355_selected_config.argtypes = [_I, _I, _I, _P, _I, _P, _I]
+    lib.sgemm_mi355_config_staging.argtypes = [_I, _I, _I, _I, _P, _I, _P, _I]
     lib.sgemm_mi355_num_configs.argtypes = []
     lib.sgemm_mi355_config_name.argtypes = [_I]
     lib.sgemm_mi355_config_name.restype = ctypes.c_char_p
@@ -89,7 +91,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                  "sgemm_mi355_select_config_ex", "sgemm_mi355_config_ops", "sgemm_mi355_splitk",
                  "sgemm_mi355_splitk_with_config", "sgemm_mi355_select_splitk",
                  "sgemm_mi355_select_config_valu", "sgemm_mi355_streamk", "sgemm_mi355_streamk_with_config",
-                 "sgemm_mi355_select_streamk", "sgemm_mi355_config_streamk"):
+                 "sgemm_mi355_select_streamk", "sgemm_mi355_config_streamk", "sgemm_mi355_selected_config",
+                 "sgemm_mi355_config_staging"):
         getattr(lib, name).restype = _I
     _lib = lib
     return lib
@@ -222,6 +225,14 @@ def sgemm_mi355_select_config(M, N, K) -> int:
     return load().sgemm_mi355_select_config(M, N, K)
 
 
+def sgemm_mi355_selected_config(M, N, K, A, lda, B, ldb) -> int:
+    return load().sgemm_mi355_selected_config(M, N, K, A, lda, B, ldb)
+
+
+def sgemm_mi355_config_staging(config, M, N, K, A, lda, B, ldb) -> int:
+    return load().sgemm_mi355_config_staging(config, M, N, K, A, lda, B, ldb)
+
+
 def sgemm_mi355_num_configs() -> int:
     return load().sgemm_mi355_num_configs()
 
@@ -273,6 +284,19 @@ def config_id(name: str) -> int:
 
 # ---- torch convenience wrapper (marshalling only) ---------------------------
 
+def _empty_on(shape, device, stream):
+    """A float32 tensor allocated with torch's caching allocator on `stream`,
+    the stream the library launches on. The allocator ties a block to the
+    stream it was allocated on and hands it out again only after the work
+    queued on that stream up to its release has run, so a temporary
+    (workspace) dropped on return cannot be reused while the kernels that
+    read or write it are still pending."""
+    import torch
+
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=torch.float32, device=device)
+
+
 def _ld(x, name):
     """Leading dimension (row stride in elements) of a 2-D tensor whose rows
     are contiguous. A dimension of size 1 may carry any stride in torch, so
@@ -307,11 +331,12 @@ def matmul(A, B, out=None, *, kind: str = "mfma", config: int | None = None, str
     K2, N = B.shape
     if K != K2:
         raise ValueError("inner dimensions differ")
+    s_obj = stream or torch.cuda.current_stream(A.device)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        out = _empty_on((M, N), A.device, s_obj)
     if out.shape != (M, N) or out.dtype != torch.float32 or not out.is_cuda:
         raise ValueError("out must be an M x N float32 GPU tensor")
-    s = (stream or torch.cuda.current_stream(A.device)).cuda_stream
+    s = s_obj.cuda_stream
     args = (M, N, K, A.data_ptr(), _ld(A, "A"), B.data_ptr(), _ld(B, "B"),
             out.data_ptr(), _ld(out, "C"), s)
     if config is not None:
@@ -345,16 +370,17 @@ def gemm(A, B, C=None, *, opA: int = OP_N, opB: int = OP_N, alpha: float = 1.0, 
     K2, N = _op_dims(B, opB)
     if K != K2:
         raise ValueError("inner dimensions differ")
+    s_obj = stream or torch.cuda.current_stream(A.device)
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs an input C")
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        C = _empty_on((M, N), A.device, s_obj)
     if tuple(C.shape) != (M, N):
         raise ValueError("C must be M x N")
     for x, n in ((A, "A"), (B, "B"), (C, "C")):
         if x.dtype != torch.float32 or not x.is_cuda:
             raise TypeError(f"{n} must be a float32 GPU tensor")
-    s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
+    s = s_obj.cuda_stream
     args = (opA, opB, M, N, K, alpha, A.data_ptr(), _ld(A, "A"), 0, B.data_ptr(), _ld(B, "B"), 0,
             beta, C.data_ptr(), _ld(C, "C"), 0, 1, s)
     rc = (sgemm_mi355_strided_batched(*args) if config is None
@@ -378,11 +404,12 @@ def gemm_strided_batched(A, B, C=None, *, opA: int = OP_N, opB: int = OP_N, alph
     K2, N = _op_dims(B[0], opB)
     if K != K2:
         raise ValueError("inner dimensions differ")
+    s_obj = stream or torch.cuda.current_stream(A.device)
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs an input C")
-        C = torch.empty((batch, M, N), dtype=torch.float32, device=A.device)
-    s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
+        C = _empty_on((batch, M, N), A.device, s_obj)
+    s = s_obj.cuda_stream
     sa = A.stride(0) if A.shape[0] > 1 else 0
     sb = B.stride(0) if B.shape[0] > 1 else 0
     args = (opA, opB, M, N, K, alpha, A.data_ptr(), _ld(A[0], "A"), sa, B.data_ptr(), _ld(B[0], "B"),
@@ -409,17 +436,18 @@ def gemm_splitk(A, B, C=None, *, splits: int | None = None, opA: int = OP_N, opB
     K2, N = _op_dims(B, opB)
     if K != K2:
         raise ValueError("inner dimensions differ")
+    s_obj = stream or torch.cuda.current_stream(A.device)
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs an input C")
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        C = _empty_on((M, N), A.device, s_obj)
     if splits is None:
         splits, suggested = sgemm_mi355_select_splitk(opA, opB, M, N, K)
         config = suggested if config is None else config
     need = sgemm_mi355_splitk_workspace_size(M, N, K, splits)
     if workspace is None:
-        workspace = torch.empty((max(need, 4) + 3) // 4, dtype=torch.float32, device=A.device)
-    s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
+        workspace = _empty_on(((max(need, 4) + 3) // 4,), A.device, s_obj)
+    s = s_obj.cuda_stream
     args = (opA, opB, M, N, K, alpha, A.data_ptr(), _ld(A, "A"), B.data_ptr(), _ld(B, "B"), beta,
             C.data_ptr(), _ld(C, "C"), splits, workspace.data_ptr(), workspace.numel() * 4, s)
     rc = (sgemm_mi355_splitk(*args) if config is None else sgemm_mi355_splitk_with_config(*args, config))
@@ -443,14 +471,15 @@ def gemm_streamk(A, B, C=None, *, opA: int = OP_N, opB: int = OP_N, alpha: float
     K2, N = _op_dims(B, opB)
     if K != K2:
         raise ValueError("inner dimensions differ")
+    s_obj = stream or torch.cuda.current_stream(A.device)
     if C is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs an input C")
-        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+        C = _empty_on((M, N), A.device, s_obj)
     need = sgemm_mi355_streamk_workspace_size(opA, opB, M, N, K, -1 if config is None else config)
     if workspace is None:
-        workspace = torch.empty((max(need, 16) + 3) // 4, dtype=torch.float32, device=A.device)
-    s = (stream or torch.cuda.current_stream(C.device)).cuda_stream
+        workspace = _empty_on(((max(need, 16) + 3) // 4,), A.device, s_obj)
+    s = s_obj.cuda_stream
     args = (opA, opB, M, N, K, alpha, A.data_ptr(), _ld(A, "A"), B.data_ptr(), _ld(B, "B"), beta,
             C.data_ptr(), _ld(C, "C"), workspace.data_ptr(), workspace.numel() * 4, s)
     rc = (sgemm_mi355_streamk(*args) if config is None else sgemm_mi355_streamk_with_config(*args, config))

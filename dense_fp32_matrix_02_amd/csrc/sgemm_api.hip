@@ -190,14 +190,17 @@ bool is_direct_config(int id) { return id >= kNumMfmaConfigs && id < kNumMfmaCon
 constexpr int kSatChains = 8;
 constexpr double kStoreDepth = 40.0;
 
+// Evaluated in double: the workgroup count (up to 2^52 tiles of 32 x 32 times
+// 65535 batch entries) can exceed int64 for shapes the selection is asked
+// about before validation.
 double busy_time(const KernelConfig& c, int occ, int M, int N, int K, int batch) {
-  const int64_t wgs = tiles_for(c, M, N) * (int64_t)(batch < kMaxGridY ? batch : kMaxGridY);
-  const int64_t n = (wgs + kCompute - 1) / kCompute;
-  if (n <= 0) return 0.0;
-  const int64_t blocks = (int64_t)(c.kgroups > 0 ? c.kgroups : 1) * (c.bm / 32) * (c.bn / 32);
-  const int64_t resident = (n < occ ? n : occ) * blocks;
-  const double stretch = resident >= kSatChains ? 1.0 : (double)kSatChains / (double)resident;
-  return (double)n * stretch * ((double)(((int64_t)K + c.bk - 1) / c.bk) + kStoreDepth / c.bk);
+  const double wgs = (double)tiles_for(c, M, N) * (double)(batch < kMaxGridY ? batch : kMaxGridY);
+  const double n = std::ceil(wgs / kCompute);
+  if (!(n > 0.0)) return 0.0;
+  const double blocks = (double)(c.kgroups > 0 ? c.kgroups : 1) * (c.bm / 32) * (c.bn / 32);
+  const double resident = (n < occ ? n : (double)occ) * blocks;
+  const double stretch = resident >= kSatChains ? 1.0 : (double)kSatChains / resident;
+  return n * stretch * ((double)(((int64_t)K + c.bk - 1) / c.bk) + kStoreDepth / c.bk);
 }
 
 const Resolved& resolved() {
@@ -271,7 +274,7 @@ int rule_select(int opA, int opB, int M, int N, int K, int batch) {
     const KernelConfig& c = *config_at(id);
     const int64_t n = tiles_for(c, M, N);
     const double fill = n > 0 ? (double)M * N / ((double)n * c.bm * c.bn) : 1.0;
-    if (n * gy >= kRuleTiles[opA][opB][i].min_wgs && fill >= kRuleMinFill) return id;
+    if ((double)n * (double)gy >= kRuleTiles[opA][opB][i].min_wgs && fill >= kRuleMinFill) return id;
   }
   return rs.small[opA][opB][K >= kRuleLongK ? 1 : 0];
 }
@@ -616,6 +619,7 @@ uint64_t streamk_bytes(const KernelConfig& c, int grid) { return 8ull * (uint64_
 // Workspace c's stream-K form needs for an M x N x K product: the larger of
 // its two kernels' needs, since alignment decides which one runs.
 uint64_t streamk_need(const KernelConfig& c, int M, int N, int K) {
+  if (tiles_for(c, M, N) > INT_MAX / 2) return 0;  // run_streamk rejects these (ERR_EXTENT)
   const int cus = device_compute_units();
   uint64_t need = 0;
   for (int d = 0; d < 2 && cus > 0 && M > 0 && N > 0 && K > 0; ++d) {
@@ -887,6 +891,22 @@ int sgemm_mi355_validate_ex(int opA, int opB, int M, int N, int K, float alpha, 
 int sgemm_mi355_select_config(int M, int N, int K) {
   if (M < 0 || N < 0 || K < 0) return SGEMM_MI355_ERR_DIM;
   return select_mfma(0, 0, M, N, K, 1);
+}
+
+int sgemm_mi355_config_staging(int config, int M, int N, int K, const float* A, int lda, const float* B,
+                               int ldb) {
+  const KernelConfig* c = config_at(config);
+  if (!c) return SGEMM_MI355_ERR_CONFIG;
+  if (M < 0 || N < 0 || K < 0) return SGEMM_MI355_ERR_DIM;
+  if (!is_direct_config(config)) return 0;
+  const Problem p{c->transA, c->transB, M, N, K, 1.0f, A, lda, 0, B, ldb, 0, 0.0f, nullptr, 0, 0, 1};
+  if (!direct_path(*c, M, N, K, operands_aligned(p))) return 0;
+  return K % c->bk == 0 ? 1 : 2;
+}
+
+int sgemm_mi355_selected_config(int M, int N, int K, const float* A, int lda, const float* B, int ldb) {
+  if (M < 0 || N < 0 || K < 0) return SGEMM_MI355_ERR_DIM;
+  return select_for(plain(M, N, K, A, lda, B, ldb, nullptr, 0));
 }
 
 int sgemm_mi355_select_config_valu(int M, int N, int K) {

@@ -293,6 +293,30 @@ int sgemm_mi355_validate_ex(int opA, int opB, int M, int N, int K, float alpha,
  */
 int sgemm_mi355_select_config(int M, int N, int K);
 
+/*
+ * Configuration id sgemm_mi355 runs for exactly these arguments (host only):
+ * the selection above with the alignment of the actual pointers and leading
+ * dimensions taken into account (16-byte aligned A and B with lda and ldb
+ * multiples of 4 may take a direct-to-LDS configuration, others take a
+ * register-staged one). The pointers are only inspected, never read.
+ * Returns SGEMM_MI355_ERR_DIM for a negative dimension.
+ */
+int sgemm_mi355_selected_config(int M, int N, int K, const float *A, int lda, const float *B, int ldb);
+
+/*
+ * How configuration `config` stages the slabs of a single product with these
+ * arguments (host only; the pointers are only inspected): 0 through
+ * registers, 1 by direct global-to-LDS loads, 2 by direct loads for the
+ * whole slabs and through registers for a partial last slab (K not a multiple
+ * of the slab depth). Direct loads need 16-byte aligned A and B, leading
+ * dimensions that are multiples of 4, K of at least one slab and, for an
+ * operand whose rows run along M or N (B, or A transposed), that extent a
+ * multiple of 4. A and B are in the layouts the configuration reads
+ * (sgemm_mi355_config_ops). Returns SGEMM_MI355_ERR_CONFIG for an unknown id,
+ * SGEMM_MI355_ERR_DIM for a negative dimension.
+ */
+int sgemm_mi355_config_staging(int config, int M, int N, int K, const float *A, int lda, const float *B, int ldb);
+
 /* Configuration id sgemm_mi355_valu uses for a problem shape (host only). */
 int sgemm_mi355_select_config_valu(int M, int N, int K);
 

@@ -58,7 +58,7 @@ def test_error_codes_match_header():
 A0, B0, C0 = 0x10000000, 0x20000000, 0x30000000
 
 
-@pytest.mark.parametrize("args,code", [
+VALIDATION_CASES = [
     ((-1, 4, 4, A0, 4, B0, 4, C0, 4), sg.ERR_DIM),
     ((4, -1, 4, A0, 4, B0, 4, C0, 4), sg.ERR_DIM),
     ((4, 4, -1, A0, 4, B0, 4, C0, 4), sg.ERR_DIM),
@@ -82,7 +82,10 @@ A0, B0, C0 = 0x10000000, 0x20000000, 0x30000000
     ((4, 4, 4, A0, 5, B0, 4, A0 + 4 * 19, 4), sg.OK),      # A extent = 3*5+4 = 19 floats
     ((4, 4, 4, A0, 5, B0, 4, A0 + 4 * 18, 4), sg.ERR_ALIAS),
     ((2 ** 31 - 1, 4, 4, A0, 4, B0, 4, C0, 4), sg.ERR_EXTENT),
-])
+]
+
+
+@pytest.mark.parametrize("args,code", VALIDATION_CASES)
 def test_validation_codes(args, code):
     assert sg.sgemm_mi355_validate(*args) == code
 
@@ -132,6 +135,57 @@ def test_selection_picks_matrix_core_configs_for_every_workload():
         cid = sg.sgemm_mi355_select_config(*shape)
         assert 0 <= cid < sg.sgemm_mi355_num_configs()
     assert sg.sgemm_mi355_select_config(-1, 1, 1) == sg.ERR_DIM
+
+
+def test_selected_config_sees_the_alignment():
+    """With 16-byte aligned operands and leading dimensions that are multiples
+    of 4, sgemm_mi355_selected_config agrees with the shape-only selection;
+    with a misaligned leading dimension it never names a direct-to-LDS
+    configuration (their direct loads need 16-byte chunks)."""
+    import workloads
+    for w in workloads.WORKLOADS:
+        sel = sg.sgemm_mi355_select_config(w.M, w.N, w.K)
+        got = sg.sgemm_mi355_selected_config(w.M, w.N, w.K, A0, w.lda, B0, w.ldb)
+        if w.lda % 4 == 0 and w.ldb % 4 == 0:
+            assert got == sel
+        else:
+            assert "_lds" not in sg.sgemm_mi355_config_name(got)
+    for (M, N, K) in [(4096, 4096, 4096), (8192, 8192, 8192), (1024, 1024, 1024)]:
+        aligned = sg.sgemm_mi355_selected_config(M, N, K, A0, K, B0, N)
+        assert aligned == sg.sgemm_mi355_select_config(M, N, K)
+        for a, lda in ((A0 + 4, K), (A0, K + 1)):
+            got = sg.sgemm_mi355_selected_config(M, N, K, a, lda, B0, N)
+            assert "_lds" not in sg.sgemm_mi355_config_name(got)
+    assert sg.sgemm_mi355_selected_config(-1, 1, 1, A0, 1, B0, 1) == sg.ERR_DIM
+
+
+def test_config_staging_follows_the_direct_load_rules():
+    """Direct loads for 16-byte aligned operands with leading dimensions that
+    are multiples of 4 and K of at least one slab (2 when K ends in a partial
+    slab); registers otherwise, and always for register-staged configurations."""
+    names = sg.config_names()
+    direct = [i for i, n in enumerate(names) if "_lds" in n]
+    assert direct
+    for cid in direct:
+        bm, bn, bk, _ = sg.sgemm_mi355_config_info(cid)
+        opA, opB = sg.sgemm_mi355_config_ops(cid)
+        M, N = bm + 4, bn + 8
+        lda = M if opA else 4 * bk
+        ldb = 4 * bk if opB else N
+        st = sg.sgemm_mi355_config_staging
+        assert st(cid, M, N, 4 * bk, A0, lda, B0, ldb) == 1
+        assert st(cid, M, N, 3 * bk + 1, A0, lda + 4, B0, ldb + 4) == 2
+        assert st(cid, M, N, bk - 1, A0, lda, B0, ldb) == 0          # less than one slab
+        assert st(cid, M, N, 4 * bk, A0 + 4, lda, B0, ldb) == 0      # 4-byte aligned base
+        assert st(cid, M, N, 4 * bk, A0, lda + 1, B0, ldb) == 0      # odd leading dimension
+        if opA:
+            assert st(cid, M + 1, N, 4 * bk, A0, lda + 4, B0, ldb) == 0  # A^T rows of M not whole chunks
+        if not opB:
+            assert st(cid, M, N + 1, 4 * bk, A0, lda, B0, ldb + 4) == 0  # B rows of N not whole chunks
+    plain = [i for i, n in enumerate(names) if "_lds" not in n]
+    assert sg.sgemm_mi355_config_staging(plain[0], 256, 256, 256, A0, 256, B0, 256) == 0
+    assert sg.sgemm_mi355_config_staging(len(names), 4, 4, 4, A0, 4, B0, 4) == sg.ERR_CONFIG
+    assert sg.sgemm_mi355_config_staging(direct[0], -1, 4, 4, A0, 4, B0, 4) == sg.ERR_DIM
 
 
 @pytest.mark.parametrize("tiles_m,tiles_n,group_m", [
