@@ -51,7 +51,7 @@ def test_workload_float(w, kind):
     C = G.gemm(A, B, kind=kind)
     A, B = np_(A), np_(B)
     assert np.isfinite(C).all()
-    if w.M * w.N * w.K <= 2 ** 30:
+    if w.M * w.N * w.K <= 10 ** 10:  # every element (the ragged workload included)
         G.check_float(C, A, B)
     else:
         G.check_float(C, A, B, rows=G.band_sample(w.M, 128, w.seed),
@@ -217,15 +217,63 @@ def test_power_of_two_scaling_is_bitwise(kind):
     np.testing.assert_array_equal(Ch, 0.5 * C)
 
 
-@pytest.mark.parametrize("w", [workloads.BY_NAME["square1024"], workloads.BY_NAME["ragged3001x2047x1537"]],
-                         ids=lambda w: w.name)
+EDGE_ALIGNED = workloads.Workload("edge4036x3972x4096", 4036, 3972, 4096, 4096, 3972, 3972, "uniform", 16)
+
+
+@pytest.mark.parametrize("w", [workloads.BY_NAME["square1024"], workloads.BY_NAME["ragged3001x2047x1537"],
+                               workloads.BY_NAME["square4096"], EDGE_ALIGNED], ids=lambda w: w.name)
 def test_repeated_runs_are_bitwise_identical(w):
+    """Ten more runs on the same float inputs give the same bits over all of C
+    (the summation order is fixed; a race between the loads of the next slab
+    and the reads of the current one would show as differences). The two
+    aligned shapes run the direct-to-LDS pipeline, the second with edge tiles
+    in M and N."""
     A, B = workloads.inputs(w)
     Ad, Bd = G.dev(A), G.dev(B)
+    cid = sg.sgemm_mi355_selected_config(w.M, w.N, w.K, Ad.data_ptr(), w.K, Bd.data_ptr(), w.N)
+    print(f"[gpu] repeated runs {w.name} config={CONFIG_NAMES[cid]}", flush=True)
+    if w.name in ("square4096", EDGE_ALIGNED.name):
+        assert sg.sgemm_mi355_config_staging(cid, w.M, w.N, w.K, Ad.data_ptr(), w.K, Bd.data_ptr(), w.N) == 1
     first = sg.matmul(Ad, Bd)
     for _ in range(10):
         again = sg.matmul(Ad, Bd)
         assert torch.equal(first, again)
+    if w is EDGE_ALIGNED:
+        C = first.cpu().numpy()
+        An, Bn = np_(A), np_(B)
+        G.check_float(C, An, Bn, rows=G.band_sample(w.M, 128, 21), cols=G.band_sample(w.N, 128, 22))
+
+
+def test_workspace_of_a_side_stream_call_outlives_the_call():
+    """Split-K and stream-K on a stream that is not the current one, the
+    wrapper allocating C and the workspace: right after the calls return, a
+    buffer of the workspace's size is allocated and filled on the current
+    stream before anything is synchronised. The workspace and C belong to the
+    launch stream's pool, so that buffer cannot be carved out of them while
+    the kernels still run, and the results stay exact."""
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    M, N, K = 96, 80, 8192
+    A, B = workloads.draw(M, N, K, 31, "int4")
+    Ad, Bd = G.dev(A), G.dev(B)
+    side.wait_stream(cur)
+    need = sg.sgemm_mi355_splitk_workspace_size(M, N, K, 8)
+    C1 = sg.gemm_splitk(Ad, Bd, splits=8, stream=side)
+    junk = torch.full((need // 4 + M * N,), 7.0, device="cuda")
+    sk_cfg = sg.config_id("mfma32_256x256x16_w4x4_lds2")
+    M2, N2, K2 = 768, 768, 2048
+    A2, B2 = workloads.draw(M2, N2, K2, 32, "int4")
+    A2d, B2d = G.dev(A2), G.dev(B2)
+    side.wait_stream(cur)
+    need2 = sg.sgemm_mi355_streamk_workspace_size(0, 0, M2, N2, K2, sk_cfg)
+    assert need2 > 0
+    C2 = sg.gemm_streamk(A2d, B2d, config=sk_cfg, stream=side)
+    junk2 = torch.full((need2 // 4 + M2 * N2,), -3.0, device="cuda")
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert float(junk[0]) == 7.0 and float(junk2[-1]) == -3.0
+    G.check_exact(C1.cpu().numpy(), np_(A), np_(B))
+    G.check_exact(C2.cpu().numpy(), np_(A2), np_(B2))
 
 
 def test_runs_on_a_side_stream():
@@ -327,3 +375,30 @@ def test_direct_lds_configs_exact(cid):
     Cs = sg.gemm_splitk(G.dev(_stored(A, opA)), G.dev(_stored(B, opB)), splits=3, opA=opA, opB=opB, config=cid)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(Cs.cpu().numpy(), oracle.sgemm_f32(np_(A), np_(B)))
+
+
+@pytest.mark.parametrize("cid", DIRECT_IDS, ids=[CONFIG_NAMES[i] for i in DIRECT_IDS])
+def test_direct_lds_partial_last_slab_any_remainder(cid):
+    """K = whole slabs plus 1 or 3 values (odd K) with the stored rows padded
+    to multiples of 4 floats, so the operands stay 16-byte aligned and the
+    configuration takes its direct path with a register-staged last slab
+    (checked through sgemm_mi355_config_staging); the element-wise tail of the
+    register loader then runs on the k-contiguous operands. Exact on integer
+    inputs, in the operand layouts the configuration reads."""
+    bm, bn, bk, _ = sg.sgemm_mi355_config_info(cid)
+    opA, opB = sg.sgemm_mi355_config_ops(cid)
+    seed = 1500
+    for slabs, r in ((1, 1), (2, 3), (3, 1), (5, 3)):
+        seed += 1
+        M, N, K = bm + 4, bn - 4, slabs * bk + r
+        A, B = workloads.draw(M, N, K, seed, "int4")
+        As, Bs = _stored(A, opA), _stored(B, opB)
+        lda = -(-As.shape[1] // 4) * 4
+        ldb = -(-Bs.shape[1] // 4) * 4
+        Ad = G.dev(workloads.embed(As, lda))[:, :As.shape[1]]
+        Bd = G.dev(workloads.embed(Bs, ldb))[:, :Bs.shape[1]]
+        assert sg.sgemm_mi355_config_staging(cid, M, N, K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb) == 2
+        print(f"[gpu] config={CONFIG_NAMES[cid]} M={M} N={N} K={K} lda={lda} ldb={ldb}", flush=True)
+        C = sg.gemm(Ad, Bd, opA=opA, opB=opB, config=cid)
+        torch.cuda.synchronize()
+        G.check_exact(C.cpu().numpy(), np_(A), np_(B))
