@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(HERE, "libsgemm_mi355.so")
 OK = 0
 ERR_DIM, ERR_LD, ERR_NULL, ERR_ALIAS, ERR_EXTENT, ERR_LAUNCH, ERR_CONFIG, ERR_ALIGN = (
     -1, -2, -3, -4, -5, -6, -7, -8)
-ERR_STRIDE, ERR_OP, ERR_WORKSPACE = -9, -10, -11
+ERR_STRIDE, ERR_OP, ERR_WORKSPACE, ERR_SCRATCH = -9, -10, -11, -12
+SCRATCH_BYTES = 32 << 20
 OP_N, OP_T = 0, 1
 
 _lib = None
@@ -56,6 +57,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sgemm_mi355_strided_batched_with_config.argtypes = _GEMM_SB + [_I]
     lib.sgemm_mi355_splitk.argtypes = _GEMM_EX[:-1] + [_I, _P, ctypes.c_size_t, _P]
     lib.sgemm_mi355_splitk_with_config.argtypes = _GEMM_EX[:-1] + [_I, _P, ctypes.c_size_t, _P, _I]
+    lib.sgemm_mi355_splitk_noalloc.argtypes = _GEMM_EX[:-1] + [_I, _P]
     lib.sgemm_mi355_splitk_workspace_size.argtypes = [_I, _I, _I, _I]
     lib.sgemm_mi355_splitk_workspace_size.restype = ctypes.c_size_t
     lib.sgemm_mi355_select_splitk.argtypes = [_I, _I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]
@@ -92,7 +94,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                  "sgemm_mi355_splitk_with_config", "sgemm_mi355_select_splitk",
                  "sgemm_mi355_select_config_valu", "sgemm_mi355_streamk", "sgemm_mi355_streamk_with_config",
                  "sgemm_mi355_select_streamk", "sgemm_mi355_config_streamk", "sgemm_mi355_selected_config",
-                 "sgemm_mi355_config_staging"):
+                 "sgemm_mi355_config_staging", "sgemm_mi355_splitk_noalloc"):
         getattr(lib, name).restype = _I
     _lib = lib
     return lib
@@ -140,6 +142,10 @@ def sgemm_mi355_splitk_with_config(opA, opB, M, N, K, alpha, A, lda, B, ldb, bet
                                    workspace, workspace_bytes, stream, config) -> int:
     return load().sgemm_mi355_splitk_with_config(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                                                  splits, workspace, workspace_bytes, stream, config)
+
+
+def sgemm_mi355_splitk_noalloc(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, splits, stream) -> int:
+    return load().sgemm_mi355_splitk_noalloc(opA, opB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, splits, stream)
 
 
 def sgemm_mi355_splitk_workspace_size(M, N, K, splits) -> int:

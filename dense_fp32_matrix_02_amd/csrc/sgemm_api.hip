@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "sgemm_internal.h"
@@ -748,6 +749,40 @@ int select_for(const Problem& p) {
                      aligned);
 }
 
+// ---- split-K without allocation -------------------------------------------
+// The partial sums of sgemm_mi355_splitk_noalloc live in this file-scope
+// device array instead of a caller workspace: every device the library runs
+// on holds one copy of SGEMM_MI355_SCRATCH_BYTES until the process ends. In
+// host code `scratch` names a host-side stand-in, not device memory; the
+// device address of each device's copy comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept in scratch_ptr.
+static __device__ __align__(256) float scratch[SGEMM_MI355_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+float* scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (device address), or an error code.
+int current_scratch(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return SGEMM_MI355_ERR_LAUNCH;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return SGEMM_MI355_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return SGEMM_MI355_ERR_LAUNCH;
+    }
+    scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = scratch_ptr[dev];
+  return SGEMM_MI355_OK;
+}
+
 }  // namespace
 }  // namespace sgemm_impl
 
@@ -816,6 +851,25 @@ int sgemm_mi355_splitk_with_config(int opA, int opB, int M, int N, int K, float 
                                    size_t workspace_bytes, hipStream_t stream, int config) {
   const Problem p{opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1};
   return run_splitk(p, C, splits, workspace, workspace_bytes, stream, config);
+}
+
+int sgemm_mi355_splitk_noalloc(int opA, int opB, int M, int N, int K, float alpha, const float* A, int lda,
+                               const float* B, int ldb, float beta, float* C, int ldc, int splits,
+                               hipStream_t stream) {
+  const Problem p{opA, opB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc, 0, 1};
+  const int v = validate(p);
+  if (v != SGEMM_MI355_OK) return v;
+  if (splits < 1 || splits > kMaxSplits) return SGEMM_MI355_ERR_DIM;
+  const SplitPlan sp = plan_splits(K, splits);
+  const int config = sp.splits > 1 ? rule_select(opA, opB, M, N, sp.kchunk, sp.splits) : select_for(p);
+  const bool uses_ab = alpha != 0.0f && K > 0 && M > 0 && N > 0;
+  const uint64_t need = uses_ab ? splitk_bytes(M, N, sp.splits) : 0;
+  if (need == 0) return run_splitk(p, C, splits, nullptr, 0, stream, config);
+  if (need > SGEMM_MI355_SCRATCH_BYTES) return SGEMM_MI355_ERR_SCRATCH;
+  float* w = nullptr;
+  const int e = current_scratch(&w);
+  if (e != SGEMM_MI355_OK) return e;
+  return run_splitk(p, C, splits, w, SGEMM_MI355_SCRATCH_BYTES, stream, config);
 }
 
 int sgemm_mi355_select_splitk(int opA, int opB, int M, int N, int K, int* splits, int* config) {
@@ -979,6 +1033,8 @@ const char* sgemm_mi355_strerror(int code) {
     case SGEMM_MI355_ERR_ALIGN: return "a matrix pointer is not 4-byte aligned";
     case SGEMM_MI355_ERR_STRIDE: return "a batch stride is negative, or batch entries of C overlap";
     case SGEMM_MI355_ERR_OP: return "an operand op is neither SGEMM_MI355_OP_N nor SGEMM_MI355_OP_T";
+    case SGEMM_MI355_ERR_SCRATCH:
+      return "the split-K partial sums exceed the library's static scratch (SGEMM_MI355_SCRATCH_BYTES per device)";
     case SGEMM_MI355_ERR_WORKSPACE:
       return "the workspace is smaller than sgemm_mi355_splitk_workspace_size or sgemm_mi355_streamk_workspace_size";
     default: return "unknown error code";

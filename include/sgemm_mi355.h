@@ -23,8 +23,10 @@
  * caller; `stream` is the caller's HIP stream (0 = the default stream). A
  * call validates its arguments on the host, enqueues one kernel on `stream`
  * and returns without synchronising; results are visible to work ordered
- * after it on that stream. The library allocates no memory, keeps no mutable
- * global state (calls are thread-safe) and never synchronises the device.
+ * after it on that stream. The library allocates no memory and never
+ * synchronises the device; its only mutable global state is the per-device
+ * address of the static scratch of sgemm_mi355_splitk_noalloc, looked up
+ * once under a lock (calls are thread-safe).
  * A kernel fault surfaces at the caller's next synchronisation.
  *
  * Precision. Products and sums are FP32 (CDNA4 FP32 matrix instructions in
@@ -61,6 +63,11 @@ extern "C" {
 #define SGEMM_MI355_ERR_STRIDE (-9)   /* a batch stride is negative, or batch entries of C overlap */
 #define SGEMM_MI355_ERR_OP (-10)      /* an op argument is neither OP_N nor OP_T */
 #define SGEMM_MI355_ERR_WORKSPACE (-11) /* split-K or stream-K workspace smaller than required */
+#define SGEMM_MI355_ERR_SCRATCH (-12) /* split-K partial sums larger than SGEMM_MI355_SCRATCH_BYTES */
+
+/* Size of the library's static device scratch (per device), used only by
+ * sgemm_mi355_splitk_noalloc. */
+#define SGEMM_MI355_SCRATCH_BYTES (32u << 20)
 
 /* Operand ops for the general entry points (row-major storage throughout). */
 #define SGEMM_MI355_OP_N 0 /* op(X) = X */
@@ -175,6 +182,28 @@ int sgemm_mi355_splitk(int opA, int opB, int M, int N, int K, float alpha,
                        const float *A, int lda, const float *B, int ldb,
                        float beta, float *C, int ldc, int splits,
                        float *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sgemm_mi355_splitk for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that forbid allocation, harnesses
+ * that forbid hipMalloc): the same computation, the same split plan and the
+ * same kernels, so the same bits, but the partial sums go to a static device
+ * array of SGEMM_MI355_SCRATCH_BYTES that the library holds on every device
+ * it runs on until the process ends, instead of a caller workspace. The call
+ * allocates nothing (no hipMalloc, no allocating library routine); its first
+ * call on a device looks the array's device address up once. Every call on
+ * one device shares that device's array: calls whose work overlaps on one
+ * device (different streams, or threads racing on one stream's enqueue order)
+ * race on it and must be ordered by the caller; calls ordered on one stream
+ * are safe. Nothing in the array needs clearing: every partial sum is
+ * written before it is read. Errors as sgemm_mi355_splitk, plus
+ * SGEMM_MI355_ERR_SCRATCH when 4 * chunks * M * N bytes of partial sums
+ * (sgemm_mi355_splitk_workspace_size) exceed SGEMM_MI355_SCRATCH_BYTES;
+ * nothing is enqueued then.
+ */
+int sgemm_mi355_splitk_noalloc(int opA, int opB, int M, int N, int K, float alpha,
+                               const float *A, int lda, const float *B, int ldb,
+                               float beta, float *C, int ldc, int splits, hipStream_t stream);
 
 /* Workspace bytes sgemm_mi355_splitk needs (0: no split, none needed). */
 size_t sgemm_mi355_splitk_workspace_size(int M, int N, int K, int splits);

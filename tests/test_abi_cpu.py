@@ -48,7 +48,7 @@ def test_error_codes_match_header():
     codes = dict((k, int(v)) for k, v in re.findall(r"#define SGEMM_MI355_(\w+) \(?(-?\d+)\)?", text))
     assert codes["OK"] == sg.OK
     for name in ("DIM", "LD", "NULL", "ALIAS", "EXTENT", "LAUNCH", "CONFIG", "ALIGN", "STRIDE", "OP",
-                 "WORKSPACE"):
+                 "WORKSPACE", "SCRATCH"):
         assert codes["ERR_" + name] == getattr(sg, "ERR_" + name)
         assert sg.strerror(codes["ERR_" + name]) != sg.strerror(12345)
     assert sg.strerror(0) == "success"
@@ -97,6 +97,23 @@ def test_entry_points_reject_before_any_hip_call(fn):
     assert f(4, 4, 5, A0, 4, B0, 4, C0, 4, 0) == sg.ERR_LD
     assert f(4, 4, 4, A0, 4, B0, 4, A0 + 8, 4, 0) == sg.ERR_ALIAS
     assert f(0, 4, 4, 0, 4, 0, 4, 0, 4, 0) == sg.OK   # quick return, nothing enqueued
+
+
+def test_splitk_noalloc_rejects_before_any_hip_call():
+    """Validation, then the size check against the static scratch, both on
+    the host: 4 chunks of 2048 x 2048 partial sums are 64 MiB."""
+    assert int(re.search(r"#define SGEMM_MI355_SCRATCH_BYTES \((\d+)u << (\d+)\)",
+                         open(os.path.join(ROOT, "include", "sgemm_mi355.h")).read()).group(1)) << 20 \
+        == sg.SCRATCH_BYTES
+    f = sg.sgemm_mi355_splitk_noalloc
+    assert f(0, 0, -1, 4, 4, 1.0, A0, 4, B0, 4, 0.0, C0, 4, 2, 0) == sg.ERR_DIM
+    assert f(0, 0, 4, 4, 4, 1.0, A0, 4, B0, 4, 0.0, C0, 4, 0, 0) == sg.ERR_DIM
+    assert f(0, 0, 4, 4, 4, 1.0, A0, 4, B0, 4, 0.0, A0 + 8, 4, 2, 0) == sg.ERR_ALIAS
+    M = N = 2048
+    K = 8192
+    assert sg.sgemm_mi355_splitk_workspace_size(M, N, K, 4) == 2 * sg.SCRATCH_BYTES
+    assert f(0, 0, M, N, K, 1.0, A0, K, B0, N, 0.0, C0 + 2 ** 30, N, 4, 0) == sg.ERR_SCRATCH
+    assert "scratch" in sg.strerror(sg.ERR_SCRATCH)
 
 
 def test_with_config_rejects_unknown_ids():
