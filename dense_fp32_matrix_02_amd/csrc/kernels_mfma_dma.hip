@@ -58,12 +58,18 @@ __device__ __forceinline__ void copy16_to_lds(const float* g, float* lds) {
 // counters at their maximum (no wait).
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Position of chunk c of a k-contiguous line r: lines two (BK = 16) or one
-// (BK >= 32) 128-byte bank spans apart get different chunk permutations, so
-// eight consecutive lines reading the same logical chunk hit distinct banks.
+// Position of chunk c of a k-contiguous line r is c ^ swz(r). gfx950's LDS
+// has 64 four-byte banks and serves a 128-bit read 16 lanes at a time, so
+// the 16 consecutive lines that 16 lanes read at one logical chunk must fall
+// in 16 different four-bank groups. A line of BK floats starts at bank
+// (r * BK) mod 64: with BK = 16 lines r and r + 4 start at the same bank, so
+// the chunk permutation changes with r / 4; with BK = 32, with r / 2; with
+// BK >= 64 every line starts at bank 0, so it changes with r. (Counter probe
+// of these read patterns: 4 LDS cycles per 64-lane 128-bit read with these
+// permutations, 8 with the permutation of every second line.)
 template <int BK>
 __device__ __forceinline__ int swz(int r) {
-  return BK == 16 ? (r >> 1) & 3 : r & 7;
+  return BK == 16 ? (r >> 2) & 3 : BK == 32 ? (r >> 1) & 7 : r & 15;
 }
 
 // One operand's slab: ROWS lines by BK k values, staged by NW waves.
@@ -79,6 +85,7 @@ struct Slab {
   static constexpr int PER_WAVE = REGIONS / NW;        // direct loads per wave per slab
   static constexpr int CHUNKS = FLOATS / 4 / NT;       // register-staged chunks per thread
   static constexpr int CPL = KCONTIG ? BK / 4 : ROWS / 4;  // 16-byte chunks per LDS row
+  static constexpr bool KC = KCONTIG;
   static_assert(!KCONTIG || BK == 16 || BK % 32 == 0, "swizzle is defined for 16-deep and 32k-deep slabs");
   static_assert(ROWS % 32 == 0 && REGIONS % NW == 0, "whole 1 KiB regions per wave");
   static_assert((FLOATS / 4) % NT == 0, "whole chunks per thread");
@@ -156,7 +163,9 @@ struct Slab {
   // Fragments. Lane (l32, h) of line block i reads line `line_w + 32 i + l32`
   // at k = kk + 4h + u, u = 0..3. For k-contiguous lines that is logical chunk
   // kk/4 + h, stored at (kk/4 + h) ^ swz(l32) (line_w and 32 i are multiples
-  // of 32); kk/4 is even, so the float offset is kk ^ key, key = 4 (h ^ swz).
+  // of 32, and swz depends on the line modulo 32); kk/4 is even, so the float
+  // offset is kk ^ key, key = 4 (h ^ swz). A k group's first k of the slab,
+  // a multiple of 32 that kk never reaches, is XORed into the key the same way.
   __device__ static const float* frag_base(const float* lds, int line_w, int l32, int h) {
     if constexpr (KCONTIG) return lds + (line_w + l32) * BK;
     else return lds + 4 * h * ROWS + line_w + l32;
@@ -192,16 +201,23 @@ struct DmaCfg {
   static constexpr int RED_PER_ARRAY =
       (SlabA::FLOATS < SlabB::FLOATS ? SlabA::FLOATS : SlabB::FLOATS) / (BM * BN);
   static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile must be 32x32 blocks");
-  static_assert(STAGES >= 2 && STAGES <= 3, "two or three LDS stages");
+  static_assert(STAGES >= 2 && STAGES <= 4, "two to four LDS stages");
   static_assert(NT <= 1024, "at most 16 waves per workgroup");
   static_assert(KG == 1 || (KSUB % 32 == 0 && KSUB * KG == BK), "each group takes whole 32-deep k ranges");
   static_assert(KG == 1 || KG - 1 <= RED_PER_ARRAY * 2 * STAGES, "group sums fit in the stage arrays");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per CU");
   // Waves per SIMD the direct kernel's registers must allow: four, or as many
   // as the workgroups that fit in LDS can bring (the unused stage arrays of a
-  // two-stage kernel take up to 2 KiB more).
+  // two-stage kernel take up to 2 KiB more), and no more than leave room for
+  // the wave's accumulators (FM x FN blocks of 16 registers) next to its
+  // fragments and addresses in the 512 registers a SIMD lane holds: 128
+  // each for four waves, 256 for two, all 512 for one (accumulators then in
+  // AGPRs).
   static constexpr int LDS_WGS = (160 * 1024) / (LDS_BYTES + 2048);
-  static constexpr int WAVES_EU = LDS_WGS * NW / 4 < 4 ? (LDS_WGS * NW / 4 > 1 ? LDS_WGS * NW / 4 : 1) : 4;
+  static constexpr int LDS_WAVES = LDS_WGS * NW / 4 < 4 ? (LDS_WGS * NW / 4 > 1 ? LDS_WGS * NW / 4 : 1) : 4;
+  static constexpr int ACC_REGS = FM * FN * 16;
+  static constexpr int REG_WAVES = ACC_REGS <= 64 ? 4 : ACC_REGS <= 160 ? 2 : 1;
+  static constexpr int WAVES_EU = LDS_WAVES < REG_WAVES ? LDS_WAVES : REG_WAVES;
 };
 
 // DIRECT: every slab by direct loads (the launcher guarantees 16-byte aligned
@@ -225,22 +241,27 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
   __shared__ __attribute__((aligned(1024))) float As0[SA::FLOATS];
   __shared__ __attribute__((aligned(1024))) float As1[SA::FLOATS];
   __shared__ __attribute__((aligned(1024))) float As2[ST > 2 ? SA::FLOATS : 4];
+  __shared__ __attribute__((aligned(1024))) float As3[ST > 3 ? SA::FLOATS : 4];
   __shared__ __attribute__((aligned(1024))) float Bs0[SB::FLOATS];
   __shared__ __attribute__((aligned(1024))) float Bs1[SB::FLOATS];
   __shared__ __attribute__((aligned(1024))) float Bs2[ST > 2 ? SB::FLOATS : 4];
+  __shared__ __attribute__((aligned(1024))) float Bs3[ST > 3 ? SB::FLOATS : 4];
   auto stage_a = [&](auto st) -> float* {
     if constexpr (decltype(st)::value == 0) return As0;
     else if constexpr (decltype(st)::value == 1) return As1;
-    else return As2;
+    else if constexpr (decltype(st)::value == 2) return As2;
+    else return As3;
   };
   auto stage_b = [&](auto st) -> float* {
     if constexpr (decltype(st)::value == 0) return Bs0;
     else if constexpr (decltype(st)::value == 1) return Bs1;
-    else return Bs2;
+    else if constexpr (decltype(st)::value == 2) return Bs2;
+    else return Bs3;
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
 
   const int M = g.M, N = g.N;
   const int K = (blockIdx.y == gridDim.y - 1) ? g.k_last : g.K;  // last split-K chunk may be short
@@ -286,7 +307,12 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
   };
 
   // ---- fragments and the inner product ------------------------------------
-  const int akey = SA::frag_key(l32, h), bkey = SB::frag_key(l32, h);
+  // Group kg multiplies k = kg*KSUB .. (kg+1)*KSUB - 1 of each slab: for a
+  // k-contiguous slab the offset goes into the fragment key (KSUB is a
+  // multiple of 32), for a line-contiguous one into the base address.
+  const int kbase = kg * Cfg::KSUB;
+  const int akey = SA::frag_key(l32, h) ^ (SA::KC ? kbase : 0);
+  const int bkey = SB::frag_key(l32, h) ^ (SB::KC ? kbase : 0);
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -295,13 +321,9 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Group kg multiplies k = kg*KSUB .. (kg+1)*KSUB - 1 of each slab; KSUB is a
-  // multiple of 32, so for k-contiguous slabs that offset commutes with the
-  // fragment swizzle.
-  const int kbase = kg * Cfg::KSUB;
   auto compute = [&](auto stage) {
-    const float* as = SA::frag_base(stage_a(stage), wm * Cfg::WTM, l32, h) + SA::k_offset(kbase, BM);
-    const float* bs = SB::frag_base(stage_b(stage), wn * Cfg::WTN, l32, h) + SB::k_offset(kbase, BN);
+    const float* as = SA::frag_base(stage_a(stage), wm * Cfg::WTM, l32, h) + (SA::KC ? 0 : SA::k_offset(kbase, BM));
+    const float* bs = SB::frag_base(stage_b(stage), wn * Cfg::WTN, l32, h) + (SB::KC ? 0 : SB::k_offset(kbase, BN));
 #pragma unroll
     for (int kk = 0; kk < Cfg::KSUB; kk += 8) {
       f32x4 af[FM], bf[FN];
@@ -328,9 +350,20 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
     // Each wave waits for its own loads of the next slab, then the barrier
     // publishes them to the workgroup. The loop is unrolled by ST so every
     // stage index is a constant.
+    // Each wave has per_slab direct loads in flight per slab; the wait
+    // before a barrier lets the loads of the slabs after the next one stay in
+    // flight (vmcnt takes an immediate, hence the cases).
+    constexpr int per_slab = SA::PER_WAVE + SB::PER_WAVE;
+    static_assert((ST - 2) * per_slab <= 15, "vmcnt field");
+    auto wait_slabs_ahead = [&](int ahead) {  // until at most `ahead` later slabs are in flight
+      if (ST > 3 && ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * per_slab));
+      else if (ST > 2 && ahead >= 1) __builtin_amdgcn_s_waitcnt(0x0F70 | per_slab);
+      else wait_loads();
+    };
     issue_direct(0, S0{});
     if (ST > 2 && nfull > 1) issue_direct(BK, S1{});
-    wait_loads();
+    if (ST > 3 && nfull > 2) issue_direct(2 * BK, S2{});
+    wait_slabs_ahead((nfull < ST - 1 ? nfull : ST - 1) - 1);
     __syncthreads();
     auto step = [&](auto cur, int s) {
       constexpr int CUR = decltype(cur)::value;
@@ -339,15 +372,9 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
       if (more) issue_direct((s + ST - 1) * BK, Next{});
       __builtin_amdgcn_sched_barrier(0);
       compute(cur);
-      if constexpr (ST == 3) {
-        // Slab s+1 must have landed; slab s+2's loads may stay in flight.
-        constexpr int per_slab = SA::PER_WAVE + SB::PER_WAVE;
-        static_assert(per_slab <= 15, "vmcnt field");
-        if (more) __builtin_amdgcn_s_waitcnt(0x0F70 | per_slab);
-        else wait_loads();
-      } else {
-        wait_loads();
-      }
+      // Slab s+1 must have landed; the slabs issued after it may stay in flight.
+      const int issued = (s + ST - 1 < nfull ? s + ST - 1 : nfull - 1);  // last slab issued
+      wait_slabs_ahead(issued - (s + 1));
       __syncthreads();
     };
     // Whole groups of ST slabs, then the remaining nfull % ST (no exit from
@@ -357,9 +384,13 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
       step(S0{}, s);
       step(S1{}, s + 1);
       if constexpr (ST > 2) step(S2{}, s + 2);
+      if constexpr (ST > 3) step(S3{}, s + 3);
     }
     if (s < nfull) step(S0{}, s);
     if (s + 1 < nfull) step(S1{}, s + 1);
+    if constexpr (ST > 3) {
+      if (s + 2 < nfull) step(S2{}, s + 2);
+    }
     if constexpr (KTAIL) {
       if (tail) {
         load_regs(nfull * BK, true);
@@ -398,7 +429,14 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
     // As0, Bs0, As1, Bs1, ... (RED_PER_ARRAY blocks of BM*BN floats each).
     auto red_block = [&](int q) -> float* {
       const int a = (q - 1) / Cfg::RED_PER_ARRAY, off = ((q - 1) % Cfg::RED_PER_ARRAY) * BM * BN;
-      float* base = a == 0 ? As0 : a == 1 ? Bs0 : a == 2 ? As1 : a == 3 ? Bs1 : a == 4 ? As2 : Bs2;
+      float* base = a == 0   ? As0
+                    : a == 1 ? Bs0
+                    : a == 2 ? As1
+                    : a == 3 ? Bs1
+                    : a == 4 ? As2
+                    : a == 5 ? Bs2
+                    : a == 6 ? As3
+                             : Bs3;
       return base + off + wt * WAVE_FLOATS + lane;
     };
     // The K loop ends with a barrier, so no wave still reads a slab.
@@ -491,6 +529,7 @@ __device__ __forceinline__ void tile_product(const GemmArgs& g, const Stages& st
                                              int K, int m0, int n0, Epi&& epi) {
   constexpr int BK = Cfg::BK, FM = Cfg::FM, FN = Cfg::FN;
   constexpr int ST = Cfg::STAGES, NW = Cfg::NW;
+  static_assert(ST <= 3, "the stream-K kernel keeps three stage arrays");
   using SA = typename Cfg::SlabA;
   using SB = typename Cfg::SlabB;
   auto stage_a = [&](auto s) -> float* { return st.a[decltype(s)::value]; };
@@ -536,7 +575,11 @@ __device__ __forceinline__ void tile_product(const GemmArgs& g, const Stages& st
   };
 
   // ---- fragments and the inner product ------------------------------------
-  const int akey = SA::frag_key(l32, h), bkey = SB::frag_key(l32, h);
+  // Group kg's first k of each slab: in the fragment key for a k-contiguous
+  // slab, in the base address for a line-contiguous one.
+  const int kbase = kg * Cfg::KSUB;
+  const int akey = SA::frag_key(l32, h) ^ (SA::KC ? kbase : 0);
+  const int bkey = SB::frag_key(l32, h) ^ (SB::KC ? kbase : 0);
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -545,13 +588,11 @@ __device__ __forceinline__ void tile_product(const GemmArgs& g, const Stages& st
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Group kg multiplies k = kg*KSUB .. (kg+1)*KSUB - 1 of each slab; KSUB is a
-  // multiple of 32, so for k-contiguous slabs that offset commutes with the
-  // fragment swizzle.
-  const int kbase = kg * Cfg::KSUB;
   auto compute = [&](auto stage) {
-    const float* as = SA::frag_base(stage_a(stage), wm * Cfg::WTM, l32, h) + SA::k_offset(kbase, Cfg::BM);
-    const float* bs = SB::frag_base(stage_b(stage), wn * Cfg::WTN, l32, h) + SB::k_offset(kbase, Cfg::BN);
+    const float* as =
+        SA::frag_base(stage_a(stage), wm * Cfg::WTM, l32, h) + (SA::KC ? 0 : SA::k_offset(kbase, Cfg::BM));
+    const float* bs =
+        SB::frag_base(stage_b(stage), wn * Cfg::WTN, l32, h) + (SB::KC ? 0 : SB::k_offset(kbase, Cfg::BN));
 #pragma unroll
     for (int kk = 0; kk < Cfg::KSUB; kk += 8) {
       f32x4 af[FM], bf[FN];
@@ -960,6 +1001,10 @@ KernelConfig kMfmaDmaConfigs[] = {
     SGEMM_MFMA_DMA_KG_OPS(32, 32, 128, 1, 1, 4, 2),
     SGEMM_MFMA_DMA_KG(32, 32, 256, 1, 1, 8, 2),
     SGEMM_MFMA_DMA_KG_OPS(32, 32, 256, 1, 1, 8, 2),
+    // deeper pipelines: loads two or three slabs ahead
+    SGEMM_MFMA_DMA_CFG(256, 256, 16, 4, 4, 1, 4, 0, 0, "_lds4"),
+    SGEMM_MFMA_DMA_CFG(64, 64, 32, 2, 2, 1, 4, 0, 0, "_lds4"),
+    SGEMM_MFMA_DMA_CFG(64, 64, 64, 2, 2, 1, 3, 0, 0, "_lds3"),
 };
 const int kNumMfmaDmaConfigs = sizeof(kMfmaDmaConfigs) / sizeof(kMfmaDmaConfigs[0]);
 
