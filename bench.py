@@ -2,10 +2,19 @@
 """Benchmark of the FP32 GEMM hot path (C = A.B, row-major) on one MI355X.
 
 One step is one call of sgemm_mi355 on resident device inputs of the named
-workload (default: square M = N = K = 8192, U[-1,1) from seed 4). Prints ONE
-JSON line with GFLOP/s (2*M*N*K per call, GPU Parallel Book ch. 9, section
-9.1), the fraction of the FP32 matrix peak, the roofline of the kernel, and
-the CPU oracle timed on this host as a reported baseline.
+workload (default: square M = N = K = 8192, U[-1,1) from seed 4); the call
+selects its kernel configuration from the actual pointers and leading
+dimensions, as any caller's would. Prints ONE JSON line with GFLOP/s
+(2*M*N*K per call, GPU Parallel Book ch. 9, section 9.1), the fraction of the
+FP32 matrix peak, the roofline of the kernel, the same figures for the other
+workloads under "also", and the CPU oracle timed on this host as a reported
+baseline.
+
+Timing: the timed calls are queued behind a spin kernel, so they run back to
+back on the GPU and the host's cost per call (a ctypes call and the HIP
+enqueue) stays out of the measurement; ms_per_step is the span of all steps
+divided by their number, and the per-launch figures come from events around
+each call, queued the same way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -69,7 +78,42 @@ def stored_traffic(workload: str, config_name: str):
     return e.get("hbm_bytes_per_launch")
 
 
-def time_gpu(w, steps: int, warmup: int, kind: str, config, warmup_ms: float = 0.0):
+_SLEEP_CYCLES_PER_US = None
+
+
+def queue_ahead(stream, us: float):
+    """Enqueue a spin kernel of about `us` microseconds on `stream`, so the
+    launches recorded after it are queued on the GPU before it ends: they then
+    run back to back, and the host's per-launch cost (a ctypes call and the
+    HIP enqueue, tens of microseconds) stays out of the timed region."""
+    import torch
+
+    global _SLEEP_CYCLES_PER_US
+    if _SLEEP_CYCLES_PER_US is None:
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        s.record()
+        torch.cuda._sleep(1_000_000)
+        e.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_US = 1_000_000 / max(s.elapsed_time(e) * 1e3, 1.0)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(_SLEEP_CYCLES_PER_US * us))
+
+
+def time_gpu(w, steps: int, warmup: int, kind: str, config, warmup_ms: float = 300.0):
+    """Time `steps` calls of the path on resident inputs of workload w.
+
+    Two timed passes, each behind queue_ahead: one pair of events around all
+    steps (ms_per_step: the span of back-to-back launches divided by their
+    number, the average launch duration including the gap between launches;
+    a rocprofv3 kernel trace of the same run gives the kernel's own duration
+    within that gap), then events around each call (the mean, least and
+    largest single launch, each with its events' own overhead, a few
+    microseconds that matter only for the smallest workloads). Without a
+    forced configuration the call is sgemm_mi355 itself (sgemm_mi355_valu for
+    the vector kind), which selects with the actual pointers and leading
+    dimensions."""
     import torch
     import dense_fp32_matrix_02_amd as sg
     import workloads
@@ -83,47 +127,96 @@ def time_gpu(w, steps: int, warmup: int, kind: str, config, warmup_ms: float = 0
     if config is not None:
         cid = config
     elif kind == "mfma":
-        cid = sg.sgemm_mi355_select_config(w.M, w.N, w.K)
+        cid = sg.sgemm_mi355_selected_config(w.M, w.N, w.K, Av.data_ptr(), w.lda, Bv.data_ptr(), w.ldb)
     else:
         cid = sg.sgemm_mi355_select_config_valu(w.M, w.N, w.K)
 
     def step():
-        sg.matmul(Av, Bv, out=Cv, kind=kind, config=cid, stream=stream)
+        sg.matmul(Av, Bv, out=Cv, kind=kind, config=config, stream=stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # Optional extra warm-up by time: the engine clock ramps up over the first
-    # tens of milliseconds of load after an idle gap.
+    # Warm-up by time as well: after an idle gap (input generation on the
+    # host) the engine clock takes tens of milliseconds of load to ramp up.
     t_warm = time.perf_counter()
     while (time.perf_counter() - t_warm) * 1e3 < warmup_ms:
-        step()
+        for _ in range(8):
+            step()
         torch.cuda.synchronize()
+    ahead_us = max(2000.0, 80.0 * steps)
+    # pass 1: back-to-back throughput
+    s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    queue_ahead(stream, ahead_us)
+    s0.record(stream)
+    for _ in range(steps):
+        step()
+    e0.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = s0.elapsed_time(e0)
+    # pass 2: single launches
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t0 = time.perf_counter()
+    queue_ahead(stream, ahead_us)
     for i in range(steps):
         starts[i].record(stream)
         step()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]  # ms
-    total_ms = starts[0].elapsed_time(ends[-1])
-    name = sg.sgemm_mi355_config_name(cid)
     return {
         "ms_per_step": total_ms / steps,
         "mean_launch_ms": sum(per_launch) / steps,
         "min_launch_ms": min(per_launch),
         "max_launch_ms": max(per_launch),
         "wall_s": wall,
-        "config_name": name,
+        "config_name": sg.sgemm_mi355_config_name(cid),
     }
 
 
-def cpu_baseline(w, seconds: float):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_gflops(w, threads: int, reps: int) -> float:
+    """The oracle on the whole of workload w (median of `reps` runs) with
+    `threads` OpenMP threads, in GFLOP/s."""
+    import numpy as np
+    import oracle
+    import workloads
+
+    A, B = workloads.inputs(w)
+    A, B = workloads.as_numpy(A), workloads.as_numpy(B)
+    out = np.empty((w.M, w.N), np.float32)
+    n0 = oracle.max_threads()
+    oracle.set_threads(threads)
+    try:
+        times = []
+        for _ in range(reps):
+            t = time.perf_counter()
+            oracle.sgemm_f32(A, B, out=out)
+            times.append(time.perf_counter() - t)
+    finally:
+        oracle.set_threads(n0)
+    times.sort()
+    return w.flops / times[len(times) // 2] / 1e9
+
+
+def cpu_baseline(w, seconds: float, others=()):
     """The oracle (plain FP32 triple loop, OpenMP over rows), untuned, timed on
-    this host on whole rows of the same workload until about `seconds` of work."""
+    this host: on whole rows of workload w until about `seconds` of work (the
+    reported value), then on every workload in `others` whole (median of 3
+    runs for those under 1e10 FLOP), and single-threaded on those under 3e9
+    FLOP."""
     import numpy as np
     import oracle
     import workloads
@@ -141,6 +234,14 @@ def cpu_baseline(w, seconds: float):
         rows_done += r
         chunk = min(chunk * 2, 512)
     gflops = 2.0 * rows_done * w.N * w.K / elapsed / 1e9
+    per_workload = []
+    for wo in others:
+        reps = 3 if wo.flops < 1e10 else 1
+        entry = {"workload": wo.name, "GFLOP/s": round(oracle_gflops(wo, threads, reps), 3),
+                 "threads": threads, "runs": reps}
+        if wo.flops < 3e9:
+            entry["GFLOP/s_1_thread"] = round(oracle_gflops(wo, 1, 3), 3)
+        per_workload.append(entry)
     return {
         "value": round(gflops, 3),
         "unit": "GFLOP/s",
@@ -148,6 +249,10 @@ def cpu_baseline(w, seconds: float):
         "kind": "oracle",
         "sample": f"first {rows_done} of {w.M} rows of C ({w.name}), {elapsed:.1f} s, "
                   f"{threads} OpenMP threads, affinity {len(os.sched_getaffinity(0))} cpus",
+        "cpu_model": cpu_model(),
+        "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS"),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "per_workload": per_workload,
     }
 
 
@@ -180,10 +285,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="square8192")
-    ap.add_argument("--also", default="square4096",
+    ap.add_argument("--also", default="square256,square1024,square4096,ragged3001x2047x1537",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--kind", default="mfma", choices=["mfma", "valu"])
     ap.add_argument("--config", default=None, help="force a kernel configuration by name")
+    ap.add_argument("--warmup-ms", type=float, default=300.0,
+                    help="extra warm-up by time before each workload's timed steps (engine clock ramp)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -211,20 +318,29 @@ def main():
     config = sg.config_id(args.config) if args.config else None
 
     log(f"[bench] {w.name} M={w.M} N={w.N} K={w.K} kind={args.kind} steps={args.steps} warmup={args.warmup}")
-    r = time_gpu(w, args.steps, args.warmup, args.kind, config)
+    peak = PEAK_MFMA_TFLOPS if args.kind == "mfma" else PEAK_VECTOR_TFLOPS
+    r = time_gpu(w, args.steps, args.warmup, args.kind, config, args.warmup_ms)
     value = w.flops / (r["ms_per_step"] * 1e-3) / 1e9          # GFLOP/s, whole job (1 GPU)
-    achieved = w.flops / (r["mean_launch_ms"] * 1e-3) / 1e12   # TFLOP/s per launch
-    log(f"[bench] {r['config_name']}: {r['ms_per_step']:.3f} ms/step, {value:.1f} GFLOP/s")
+    achieved = w.flops / (r["ms_per_step"] * 1e-3) / 1e12      # TFLOP/s per launch (back-to-back span)
+    log(f"[bench] {r['config_name']}: {r['ms_per_step']:.4f} ms/step, {value:.1f} GFLOP/s, "
+        f"mean launch {r['mean_launch_ms']:.4f} ms")
 
     also = []
-    for name in [s for s in args.also.split(",") if s and s != w.name]:
-        wa = workloads.BY_NAME[name]
-        ra = time_gpu(wa, max(args.steps, 20), args.warmup, args.kind, None, warmup_ms=300.0)
+    others = [workloads.BY_NAME[n] for n in args.also.split(",") if n and n != w.name]
+    for wa in others:
+        ra = time_gpu(wa, max(args.steps, 20), args.warmup, args.kind, None, args.warmup_ms)
         va = wa.flops / (ra["ms_per_step"] * 1e-3) / 1e9
-        also.append({"workload": wa.name, "value": round(va, 1), "unit": "GFLOP/s",
-                     "ms_per_step": round(ra["ms_per_step"], 4), "config": ra["config_name"],
-                     "frac_fp32_mfma_peak": round(va / (PEAK_MFMA_TFLOPS * 1e3), 4)})
-        log(f"[bench] also {wa.name}: {va:.1f} GFLOP/s ({ra['config_name']})")
+        ka = wa.flops / (ra["ms_per_step"] * 1e-3) / 1e12
+        also.append({"workload": wa.name, "M": wa.M, "N": wa.N, "K": wa.K, "value": round(va, 1),
+                     "unit": "GFLOP/s", "ms_per_step": round(ra["ms_per_step"], 5), "kernel": ra["config_name"],
+                     "event_launch_ms": round(ra["mean_launch_ms"], 5),
+                     "event_launch_min_ms": round(ra["min_launch_ms"], 5),
+                     "frac_fp32_mfma_peak": round(va / (PEAK_MFMA_TFLOPS * 1e3), 4),
+                     "frac_fp32_vector_peak": round(va / (PEAK_VECTOR_TFLOPS * 1e3), 4),
+                     "launch_tflops": round(ka, 2), "launch_frac": round(ka / peak, 4),
+                     "traffic": stored_traffic(wa.name, ra["config_name"])})
+        log(f"[bench] also {wa.name}: {va:.1f} GFLOP/s, {ra['ms_per_step'] * 1e3:.2f} us per launch "
+            f"({ra['config_name']})")
 
     traffic = stored_traffic(w.name, r["config_name"])
     out = {
@@ -249,22 +365,23 @@ def main():
         "roofline": {
             "bound": "mfma" if args.kind == "mfma" else "alu",
             "achieved": round(achieved, 2),
-            "peak": PEAK_MFMA_TFLOPS if args.kind == "mfma" else PEAK_VECTOR_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_MFMA_TFLOPS, 4),
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel": r["config_name"],
-            "mean_launch_ms": round(r["mean_launch_ms"], 4),
-            "min_launch_ms": round(r["min_launch_ms"], 4),
-            "max_launch_ms": round(r["max_launch_ms"], 4),
+            "launch_ms": round(r["ms_per_step"], 4),
+            "event_launch_ms": round(r["mean_launch_ms"], 4),
+            "event_launch_min_ms": round(r["min_launch_ms"], 4),
+            "event_launch_max_ms": round(r["max_launch_ms"], 4),
             "algorithmic_flops_per_launch": w.flops,
             "min_bytes_per_launch": w.min_bytes,
         },
         "also": also,
     }
     if not args.no_cpu_baseline:
-        log(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f} s")
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        log(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f} s, then on the other workloads")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, others)
     print(json.dumps(out), flush=True)
 
 
