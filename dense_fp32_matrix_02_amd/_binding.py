@@ -48,6 +48,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             f"{path} is missing: build it with `python -m dense_fp32_matrix_02_amd.build` "
             "(the GEMM has no non-HIP implementation)")
+    # The library needs libamdhip64.so.7, and torch carries its own copy of the
+    # HIP runtime under that soname. With torch loaded first the library binds
+    # to torch's copy, so torch's streams and memory are valid for it; loaded
+    # the other way round, torch would bring a second runtime into the process
+    # and every launch on one of its streams would be rejected.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     lib.sgemm_mi355.argtypes = _GEMM
     lib.sgemm_mi355_valu.argtypes = _GEMM
