@@ -66,6 +66,22 @@ __device__ __forceinline__ f32x4 ldg4(const float* p) {
 
 enum Layout { KC = 0, MC = 1, KM = 2 };
 
+// A line-contiguous chunk that crosses the end of its line (valid < 4 of its
+// values inside the matrix) is read as the line's last whole chunk, which ends
+// at the same place, so every lane issues the same 16-byte load. This moves
+// the lane's `valid` values from the end of that chunk to the front and zeroes
+// the rest; valid >= 4 keeps v, valid <= 0 gives zeros. It runs when the chunk
+// is stored to LDS, not after the load, so the load stays in flight during
+// the slab's MFMAs.
+__device__ __forceinline__ f32x4 line_end_chunk(f32x4 v, int valid) {
+  f32x4 r;
+  r[0] = valid >= 4 ? v[0] : valid == 3 ? v[1] : valid == 2 ? v[2] : valid == 1 ? v[3] : 0.0f;
+  r[1] = valid >= 4 ? v[1] : valid == 3 ? v[2] : valid == 2 ? v[3] : 0.0f;
+  r[2] = valid >= 4 ? v[2] : valid == 3 ? v[3] : 0.0f;
+  r[3] = valid >= 4 ? v[3] : 0.0f;
+  return r;
+}
+
 // One operand of the block tile: ROWS lines by BK values of k per slab,
 // loaded by NT threads. A "line" of the loader is a row of the KC source, a
 // k-row of the MC source, or a group of four k of the KM source.
@@ -88,6 +104,10 @@ struct Operand {
   int line0;  // first line of this thread
   int col;    // KC: float4 index along k; MC: float4 index along lines; KM: line
   int valid;  // MC: lines of this thread's float4 chunk that lie inside the matrix
+  // MC, uniform over the workgroup: 0 when every chunk of the tile lies inside
+  // the matrix, 1 when some cross its end and R >= 4 (read as the line's last
+  // whole chunk), 2 when R < 4 (read value by value).
+  int edge;
   f32x4 reg[PASSES];
 
   // base: the operand of this batch entry; r0: first line of the block tile;
@@ -97,6 +117,7 @@ struct Operand {
     col = t % TPL;
     line0 = t / TPL;
     valid = R - (r0 + 4 * col);
+    edge = r0 + ROWS <= R ? 0 : (R >= 4 ? 1 : 2);
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       int line = line0 + p * LPP;
@@ -106,7 +127,9 @@ struct Operand {
         row = row < R ? row : R - 1;
         src[p] = base + (int64_t)row * ld + 4 * col;
       } else if constexpr (L == MC) {
-        src[p] = base + (int64_t)line * ld + (valid > 0 ? r0 + 4 * col : 0);
+        int c0 = r0 + 4 * col;
+        if (valid < 4) c0 = R >= 4 ? R - 4 : (valid > 0 ? c0 : 0);
+        src[p] = base + (int64_t)line * ld + c0;
       } else {
         const int c = r0 + col < R ? r0 + col : R - 1;
         src[p] = base + (int64_t)(4 * line) * ld + c;
@@ -135,8 +158,8 @@ struct Operand {
         const int kr = k0 + line;
         if (TAIL && kr >= K) {
           reg[p] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        } else if (valid >= 4) {
-          reg[p] = ldg4(s);
+        } else if (edge != 2) {
+          reg[p] = ldg4(s);  // put in place by store() when edge == 1
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) reg[p][e] = (e < valid) ? s[e] : 0.0f;
@@ -155,7 +178,8 @@ struct Operand {
       const int line = line0 + p * LPP;
       if (PARTIAL && p == PASSES - 1 && line >= LINES) break;
       float* d = (L == KM) ? lds + col * S + 4 * line : lds + line * S + 4 * col;
-      *reinterpret_cast<f32x4*>(d) = reg[p];
+      if (L == MC && edge == 1) *reinterpret_cast<f32x4*>(d) = line_end_chunk(reg[p], valid);
+      else *reinterpret_cast<f32x4*>(d) = reg[p];
     }
   }
 

@@ -41,6 +41,21 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
 
+// A line-contiguous chunk that crosses the end of its line (valid < 4 of its
+// values inside the matrix) is read as the line's last whole chunk, which ends
+// at the same place. This moves the lane's `valid` values from the end of that
+// chunk to the front and zeroes the rest; valid >= 4 keeps v, valid <= 0
+// gives zeros. It runs when the chunk is stored to LDS, so the load stays in
+// flight until then.
+__device__ __forceinline__ f32x4 line_end_chunk(f32x4 v, int valid) {
+  f32x4 r;
+  r[0] = valid >= 4 ? v[0] : valid == 3 ? v[1] : valid == 2 ? v[2] : valid == 1 ? v[3] : 0.0f;
+  r[1] = valid >= 4 ? v[1] : valid == 3 ? v[2] : valid == 2 ? v[3] : 0.0f;
+  r[2] = valid >= 4 ? v[2] : valid == 3 ? v[3] : 0.0f;
+  r[3] = valid >= 4 ? v[3] : 0.0f;
+  return r;
+}
+
 __device__ __forceinline__ f32x4 load16(const float* p) {
   f32x4 v;
   __builtin_memcpy(&v, p, sizeof(v));
@@ -135,10 +150,16 @@ struct Slab {
         const int kr = k0 + idx / CPL;
         const int col = line0 + 4 * (idx % CPL);
         const int valid = extent - col;
-        const float* s = X + (int64_t)kr * ld + (valid > 0 ? col : 0);
+        // In a tile that crosses the end of the lines (and lines of at least
+        // 4 values), a chunk that crosses it is read as the line's last whole
+        // chunk, so every lane issues one 16-byte load; store() puts the
+        // lane's values in place.
+        const bool inside = line0 + ROWS <= extent;
+        const int c0 = (valid >= 4 || inside) ? col : (extent >= 4 ? extent - 4 : (valid > 0 ? col : 0));
+        const float* s = X + (int64_t)kr * ld + c0;
         if (tail && kr >= K) {
           r[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        } else if (valid >= 4) {
+        } else if (inside || extent >= 4) {
           r[c] = load16(s);
         } else {
 #pragma unroll
@@ -147,7 +168,8 @@ struct Slab {
       }
     }
   }
-  __device__ static void store(float* lds, const f32x4 (&r)[CHUNKS], int t) {
+  // line0 and extent as given to load().
+  __device__ static void store(float* lds, const f32x4 (&r)[CHUNKS], int line0, int extent, int t) {
 #pragma unroll
     for (int c = 0; c < CHUNKS; ++c) {
       const int idx = c * NT + t;
@@ -155,7 +177,11 @@ struct Slab {
         const int line = idx / CPL;
         *reinterpret_cast<f32x4*>(lds + line * BK + 4 * ((idx % CPL) ^ swz<BK>(line))) = r[c];
       } else {
-        *reinterpret_cast<f32x4*>(lds + (idx / CPL) * ROWS + 4 * (idx % CPL)) = r[c];
+        float* d = lds + (idx / CPL) * ROWS + 4 * (idx % CPL);
+        if (line0 + ROWS > extent && extent >= 4)
+          *reinterpret_cast<f32x4*>(d) = line_end_chunk(r[c], extent - (line0 + 4 * (idx % CPL)));
+        else
+          *reinterpret_cast<f32x4*>(d) = r[c];
       }
     }
   }
@@ -302,8 +328,8 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
     SB::load(rb, B, g.ldb, n0, N, K, k0, tail, t);
   };
   auto store_regs = [&](auto stage) {
-    SA::store(stage_a(stage), ra, t);
-    SB::store(stage_b(stage), rb, t);
+    SA::store(stage_a(stage), ra, m0, M, t);
+    SB::store(stage_b(stage), rb, n0, N, t);
   };
 
   // ---- fragments and the inner product ------------------------------------
@@ -570,8 +596,8 @@ __device__ __forceinline__ void tile_product(const GemmArgs& g, const Stages& st
     SB::load(rb, B, g.ldb, n0, N, K, k0, tail, t);
   };
   auto store_regs = [&](auto stage) {
-    SA::store(stage_a(stage), ra, t);
-    SB::store(stage_b(stage), rb, t);
+    SA::store(stage_a(stage), ra, m0, M, t);
+    SB::store(stage_b(stage), rb, n0, N, t);
   };
 
   // ---- fragments and the inner product ------------------------------------

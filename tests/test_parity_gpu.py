@@ -75,7 +75,9 @@ def test_workload_integer_exact(w, kind):
 # --------------------------------------------------------------- every config, every edge
 
 def _edge_sizes(tile):
-    return sorted({1, 2, 3, tile - 1, tile, tile + 1, 2 * tile + 3})
+    # tile - 1, tile + 1, tile + 2 and 2 * tile + 3 leave 3, 1, 2 and 3 values
+    # of the last 4-value chunk of a line inside the matrix.
+    return sorted({1, 2, 3, tile - 1, tile, tile + 1, tile + 2, 2 * tile + 3})
 
 
 def _stored(X, op):
