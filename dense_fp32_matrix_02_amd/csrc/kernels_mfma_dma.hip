@@ -260,8 +260,8 @@ struct DmaCfg {
 
 // One wave per SIMD (2 x 2 waves of 128 x 128) with a hand-ordered slab loop
 // (see the SCHED branch of the kernel).
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
-struct DmaSchedCfg : DmaCfg<BM_, BN_, BK_, WM_, WN_, 2, 0, 0, 1> {
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int TA_ = 0, int TB_ = 0>
+struct DmaSchedCfg : DmaCfg<BM_, BN_, BK_, WM_, WN_, 2, TA_, TB_, 1> {
   static constexpr bool SCHED = true;
 };
 
@@ -1085,11 +1085,16 @@ hipError_t launch_mfma_dma_streamk(const GemmArgs& g, const StreamKPlan& plan, i
    reinterpret_cast<const void*>(&mfma_dma_kernel<DmaCfg<BM, BN, BK, WM, WN, ST, TA, TB, KG>, true>), KG, \
    nullptr, {nullptr, nullptr}}
 // The one-wave-per-SIMD tile with the hand-ordered slab loop.
-#define SGEMM_MFMA_DMA_SCHED(BM, BN, BK, WM, WN)                                                           \
-  {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_lds2_sched", KIND_MFMA, BM, BN, BK, 64 * WM * WN, 0, 0,      \
-   &launch_mfma_dma<DmaSchedCfg<BM, BN, BK, WM, WN>>,                                                      \
-   reinterpret_cast<const void*>(&mfma_dma_kernel<DmaSchedCfg<BM, BN, BK, WM, WN>, true>), 1, nullptr,     \
-   {nullptr, nullptr}}
+#define SGEMM_MFMA_DMA_SCHED_CFG(BM, BN, BK, WM, WN, TA, TB, SFX)                                          \
+  {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_lds2_sched" SFX, KIND_MFMA, BM, BN, BK, 64 * WM * WN, TA, TB, \
+   &launch_mfma_dma<DmaSchedCfg<BM, BN, BK, WM, WN, TA, TB>>,                                              \
+   reinterpret_cast<const void*>(&mfma_dma_kernel<DmaSchedCfg<BM, BN, BK, WM, WN, TA, TB>, true>), 1,      \
+   nullptr, {nullptr, nullptr}}
+#define SGEMM_MFMA_DMA_SCHED(BM, BN, BK, WM, WN) SGEMM_MFMA_DMA_SCHED_CFG(BM, BN, BK, WM, WN, 0, 0, "")
+#define SGEMM_MFMA_DMA_SCHED_OPS(BM, BN, BK, WM, WN)                  \
+  SGEMM_MFMA_DMA_SCHED_CFG(BM, BN, BK, WM, WN, 1, 0, "_tn"),          \
+      SGEMM_MFMA_DMA_SCHED_CFG(BM, BN, BK, WM, WN, 0, 1, "_nt"),      \
+      SGEMM_MFMA_DMA_SCHED_CFG(BM, BN, BK, WM, WN, 1, 1, "_tt")
 // The same with a stream-K form (configurations without k groups).
 #define SGEMM_MFMA_DMA_SK_CFG(BM, BN, BK, WM, WN, ST, TA, TB, SFX)                                         \
   {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SFX, KIND_MFMA, BM, BN, BK, 64 * WM * WN, TA, TB,        \
@@ -1133,6 +1138,7 @@ KernelConfig kMfmaDmaConfigs[] = {
     SGEMM_MFMA_DMA_CFG(64, 64, 32, 2, 2, 1, 4, 0, 0, "_lds4"),
     SGEMM_MFMA_DMA_CFG(64, 64, 64, 2, 2, 1, 3, 0, 0, "_lds3"),
     SGEMM_MFMA_DMA_SCHED(256, 256, 32, 2, 2),
+    SGEMM_MFMA_DMA_SCHED_OPS(256, 256, 32, 2, 2),
 };
 const int kNumMfmaDmaConfigs = sizeof(kMfmaDmaConfigs) / sizeof(kMfmaDmaConfigs[0]);
 
