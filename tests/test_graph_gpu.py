@@ -167,3 +167,25 @@ def test_graph_direct_lds_kernels():
     want = oracle.sgemm_f32(np.ascontiguousarray(At.T), np.ascontiguousarray(Bt.T))
     nan = torch.full((M, N), float("nan"), device="cuda")
     _replay_and_check(graph, C, nan, want, "direct k-group tt")
+
+
+def test_graph_hand_ordered_tile():
+    """The one-wave-per-SIMD tile under capture, plain and with both operands
+    transposed: its loads, fragment reads and barrier are ordered by hand,
+    and every replay must still give the oracle's bits."""
+    M, N, K = 768, 520, 1024
+    A, B = _ints(M, K, 93), _ints(K, N, 94)
+    cid = sg.config_id("mfma32_256x256x32_w2x2_lds2_sched")
+    Ad, Bd = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    C = torch.empty((M, N), device="cuda")
+    print(f"[gpu] graph hand-ordered tile M={M} N={N} K={K}", flush=True)
+    graph = _capture(lambda: sg.gemm(Ad, Bd, C, config=cid))
+    nan = torch.full((M, N), float("nan"), device="cuda")
+    _replay_and_check(graph, C, nan, oracle.sgemm_f32(A, B), "hand-ordered tile")
+
+    cid = sg.config_id("mfma32_256x256x32_w2x2_lds2_sched_tt")
+    At, Bt = _ints(K, M, 95), _ints(N, K, 96)
+    Ad, Bd = torch.from_numpy(At).cuda(), torch.from_numpy(Bt).cuda()
+    graph = _capture(lambda: sg.gemm(Ad, Bd, C, opA=1, opB=1, config=cid))
+    want = oracle.sgemm_f32(np.ascontiguousarray(At.T), np.ascontiguousarray(Bt.T))
+    _replay_and_check(graph, C, nan, want, "hand-ordered tile tt")
