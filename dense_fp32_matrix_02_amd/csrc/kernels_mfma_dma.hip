@@ -83,6 +83,10 @@ __device__ __forceinline__ void copy16_to_lds(const float* g, float* lds) {
 // direct loads count there too). Encoded s_waitcnt: vmcnt = 0, the other
 // counters at their maximum (no wait).
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// The s_waitcnt immediate that waits until at most n (< 64) vector memory
+// loads of this wave are in flight: vmcnt's low four bits sit in bits 3:0 of
+// the immediate and its high two in bits 15:14.
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // Position of chunk c of a k-contiguous line r is c ^ swz(r). gfx950's LDS
 // has 64 four-byte banks and serves a 128-bit read 16 lanes at a time, so
@@ -260,8 +264,8 @@ struct DmaCfg {
 
 // One wave per SIMD (2 x 2 waves of 128 x 128) with a hand-ordered slab loop
 // (see the SCHED branch of the kernel).
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int TA_ = 0, int TB_ = 0>
-struct DmaSchedCfg : DmaCfg<BM_, BN_, BK_, WM_, WN_, 2, TA_, TB_, 1> {
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int TA_ = 0, int TB_ = 0, int ST_ = 2>
+struct DmaSchedCfg : DmaCfg<BM_, BN_, BK_, WM_, WN_, ST_, TA_, TB_, 1> {
   static constexpr bool SCHED = true;
 };
 
@@ -399,17 +403,12 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
     // before a barrier lets the loads of the slabs after the next one stay in
     // flight (vmcnt takes an immediate, hence the cases).
     constexpr int per_slab = SA::PER_WAVE + SB::PER_WAVE;
-    static_assert((ST - 2) * per_slab <= 15, "vmcnt field");
+    static_assert(Cfg::SCHED || (ST - 2) * per_slab <= 15, "vmcnt field");
     auto wait_slabs_ahead = [&](int ahead) {  // until at most `ahead` later slabs are in flight
       if (ST > 3 && ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * per_slab));
       else if (ST > 2 && ahead >= 1) __builtin_amdgcn_s_waitcnt(0x0F70 | per_slab);
       else wait_loads();
     };
-    issue_direct(0, S0{});
-    if (ST > 2 && nfull > 1) issue_direct(BK, S1{});
-    if (ST > 3 && nfull > 2) issue_direct(2 * BK, S2{});
-    wait_slabs_ahead((nfull < ST - 1 ? nfull : ST - 1) - 1);
-    __syncthreads();
     if constexpr (Cfg::SCHED) {
       // One wave per SIMD, so nothing else fills the matrix pipe while this
       // wave waits: slab s is multiplied in G groups of FM x FN MFMAs, and
@@ -419,17 +418,38 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
       // next fragment set's LDS reads (double-buffered in registers). The barrier that
       // publishes slab s+1 comes two groups before the end of slab s (its
       // last LDS reads were issued earlier), and slab s+1's first fragments
-      // are read while those two groups run. sched_barrier keeps this order.
-      // The last slab reloads itself into the other stage instead of loading
-      // past K, so the loop has no branch (a branch makes the compiler wait
-      // for every LDS read at the join); those loads complete before the
-      // slab's barrier like any other.
-      static_assert(ST == 2 && Cfg::KG == 1 && (BK / 8) % 2 == 0, "scheduled loop: two stages, no k groups");
+      // are read while those two groups run (four when a group is a single
+      // MFMA). sched_barrier keeps this order.
+      // With ST stages the loads go ST - 1 slabs ahead, into the stage slab
+      // s - 1 has just left, and the barrier waits only for slab s + 1. A
+      // load past the last slab reloads the last slab instead, so every wave
+      // issues the same loads in every step (the vmcnt waits count them) and
+      // the loop has no branch (a branch makes the compiler wait for every
+      // LDS read at the join); those loads complete before a barrier like any
+      // other. A wave with a single 32 x 32 block keeps two accumulator
+      // chains (even and odd k steps), so that no MFMA waits for the one
+      // before it; they are added after the loop.
+      static_assert(Cfg::KG == 1 && (BK / 8) % 2 == 0, "scheduled loop: no k groups, an even number of fragment sets");
       constexpr int KK = BK / 8;                       // fragment sets per slab, 8 k each
       constexpr int G = 4 * KK;                        // MFMA groups per slab
       constexpr int NL = SA::PER_WAVE + SB::PER_WAVE;  // this wave's direct loads per slab
       constexpr int LG = G / 4;                        // groups that issue them
+      // The barrier group: after the slab's last LDS reads (issued in group
+      // G - 7) and while the set the next slab's first reads go to is free
+      // (from group G - 4 on); with one MFMA per group, four groups leave
+      // time for those reads to land.
+      constexpr int BAR_G = FM * FN >= 4 ? G - 2 : G - 4;
       constexpr int PER_G = (NL + LG - 1) / LG;
+      constexpr int NACC = FM * FN == 1 ? 2 : 1;
+      f32x16 acc2[NACC == 2 ? FM : 1][NACC == 2 ? FN : 1];
+      if constexpr (NACC == 2) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc2[i][j][r] = 0.0f;
+      }
       f32x4 af[2][FM], bf[2][FN];
       auto read_set = [&](auto stage, auto set, int kk) __attribute__((always_inline)) {
         constexpr int SET = decltype(set)::value;
@@ -451,7 +471,9 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
       auto group = [&](auto cur, auto gi_c, int k1) __attribute__((always_inline)) {
         constexpr int gi = decltype(gi_c)::value;
         constexpr int kk = gi / 4, u = gi % 4, set = kk & 1;
-        using Next = std::integral_constant<int, 1 - decltype(cur)::value>;
+        constexpr int CUR = decltype(cur)::value;
+        using Next = std::integral_constant<int, (CUR + ST - 1) % ST>;       // where slab s + ST - 1 goes
+        using Following = std::integral_constant<int, (CUR + 1) % ST>;       // where slab s + 1 is
         // The next set is read one group into this one: the compiler waits for
         // every outstanding LDS read before the next group that uses a set, so
         // reads issued right before such a group would stall it.
@@ -460,31 +482,64 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
 #pragma unroll
           for (int q = gi * PER_G; q < (gi + 1) * PER_G && q < NL; ++q) issue_one(q, k1, Next{});
         }
-        if constexpr (gi == G - 2) {
-          wait_loads();
+        if constexpr (gi == BAR_G) {
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm((ST - 2) * NL));  // slab s + 1 has landed
           __syncthreads();
-          read_set(Next{}, Z{}, 0);
+          read_set(Following{}, Z{}, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[set][i][u], bf[set][j][u], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < FN; ++j) {
+            if constexpr (NACC == 2 && (u & 1))
+              acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[set][i][u], bf[set][j][u], acc2[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[set][i][u], bf[set][j][u], acc[i][j], 0, 0, 0);
+          }
         __builtin_amdgcn_sched_barrier(0);
       };
       auto sched_step = [&](auto cur, int s) __attribute__((always_inline)) {
-        const int k1 = (s + 1 < nfull ? s + 1 : s) * BK;
+        const int k1 = (s + ST - 1 < nfull ? s + ST - 1 : nfull - 1) * BK;
         static_for<G>([&](auto gi_c) __attribute__((always_inline)) { group(cur, gi_c, k1); });
       };
+      static_assert((ST - 2) * NL < 64, "vmcnt field");
+      // slabs 0 .. ST-2 (a slab past the last reloads the last one)
+      static_for<ST - 1>([&](auto i_c) __attribute__((always_inline)) {
+        constexpr int i = decltype(i_c)::value;
+        const int k0 = (i < nfull ? i : nfull - 1) * BK;
+#pragma unroll
+        for (int q = 0; q < NL; ++q) issue_one(q, k0, std::integral_constant<int, i>{});
+      });
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((ST - 2) * NL));  // slab 0 has landed
+      __syncthreads();
       read_set(S0{}, Z{}, 0);
       int s = 0;
-      for (; s + 2 <= nfull; s += 2) {
+      for (; s + ST <= nfull; s += ST) {
         sched_step(S0{}, s);
         sched_step(S1{}, s + 1);
+        if constexpr (ST > 2) sched_step(S2{}, s + 2);
+        if constexpr (ST > 3) sched_step(S3{}, s + 3);
       }
       if (s < nfull) sched_step(S0{}, s);
+      if constexpr (ST > 2) {
+        if (s + 1 < nfull) sched_step(S1{}, s + 1);
+      }
+      if constexpr (ST > 3) {
+        if (s + 2 < nfull) sched_step(S2{}, s + 2);
+      }
+      if constexpr (NACC == 2) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] += acc2[i][j];
+      }
     } else {
+    issue_direct(0, S0{});
+    if (ST > 2 && nfull > 1) issue_direct(BK, S1{});
+    if (ST > 3 && nfull > 2) issue_direct(2 * BK, S2{});
+    wait_slabs_ahead((nfull < ST - 1 ? nfull : ST - 1) - 1);
+    __syncthreads();
     auto step = [&](auto cur, int s) {
       constexpr int CUR = decltype(cur)::value;
       using Next = std::integral_constant<int, (CUR + ST - 1) % ST>;
@@ -1091,6 +1146,17 @@ hipError_t launch_mfma_dma_streamk(const GemmArgs& g, const StreamKPlan& plan, i
    reinterpret_cast<const void*>(&mfma_dma_kernel<DmaSchedCfg<BM, BN, BK, WM, WN, TA, TB>, true>), 1,      \
    nullptr, {nullptr, nullptr}}
 #define SGEMM_MFMA_DMA_SCHED(BM, BN, BK, WM, WN) SGEMM_MFMA_DMA_SCHED_CFG(BM, BN, BK, WM, WN, 0, 0, "")
+// ST stages (the name then reads _lds<ST>_sched), for each op pair.
+#define SGEMM_MFMA_DMA_SCHED_ST_CFG(BM, BN, BK, WM, WN, ST, TA, TB, SFX)                                     \
+  {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_lds" #ST "_sched" SFX, KIND_MFMA, BM, BN, BK, 64 * WM * WN, \
+   TA, TB, &launch_mfma_dma<DmaSchedCfg<BM, BN, BK, WM, WN, TA, TB, ST>>,                                     \
+   reinterpret_cast<const void*>(&mfma_dma_kernel<DmaSchedCfg<BM, BN, BK, WM, WN, TA, TB, ST>, true>), 1,     \
+   nullptr, {nullptr, nullptr}}
+#define SGEMM_MFMA_DMA_SCHED_ST(BM, BN, BK, WM, WN, ST) SGEMM_MFMA_DMA_SCHED_ST_CFG(BM, BN, BK, WM, WN, ST, 0, 0, "")
+#define SGEMM_MFMA_DMA_SCHED_ST_OPS(BM, BN, BK, WM, WN, ST)                  \
+  SGEMM_MFMA_DMA_SCHED_ST_CFG(BM, BN, BK, WM, WN, ST, 1, 0, "_tn"),          \
+      SGEMM_MFMA_DMA_SCHED_ST_CFG(BM, BN, BK, WM, WN, ST, 0, 1, "_nt"),      \
+      SGEMM_MFMA_DMA_SCHED_ST_CFG(BM, BN, BK, WM, WN, ST, 1, 1, "_tt")
 #define SGEMM_MFMA_DMA_SCHED_OPS(BM, BN, BK, WM, WN)                  \
   SGEMM_MFMA_DMA_SCHED_CFG(BM, BN, BK, WM, WN, 1, 0, "_tn"),          \
       SGEMM_MFMA_DMA_SCHED_CFG(BM, BN, BK, WM, WN, 0, 1, "_nt"),      \
@@ -1139,6 +1205,10 @@ KernelConfig kMfmaDmaConfigs[] = {
     SGEMM_MFMA_DMA_CFG(64, 64, 64, 2, 2, 1, 3, 0, 0, "_lds3"),
     SGEMM_MFMA_DMA_SCHED(256, 256, 32, 2, 2),
     SGEMM_MFMA_DMA_SCHED_OPS(256, 256, 32, 2, 2),
+    SGEMM_MFMA_DMA_SCHED_ST(64, 64, 32, 2, 2, 4),
+    SGEMM_MFMA_DMA_SCHED_ST_OPS(64, 64, 32, 2, 2, 4),
+    SGEMM_MFMA_DMA_SCHED_ST(64, 64, 64, 2, 2, 3),
+    SGEMM_MFMA_DMA_SCHED_ST_OPS(64, 64, 64, 2, 2, 3),
 };
 const int kNumMfmaDmaConfigs = sizeof(kMfmaDmaConfigs) / sizeof(kMfmaDmaConfigs[0]);
 
