@@ -48,13 +48,22 @@ typedef __attribute__((address_space(1))) void global_void;
 // chunk to the front and zeroes the rest; valid >= 4 keeps v, valid <= 0
 // gives zeros. It runs when the chunk is stored to LDS, so the load stays in
 // flight until then.
+// Written as single selects of plain values: nested conditionals on vector
+// elements compiled to divergent branches.
 __device__ __forceinline__ f32x4 line_end_chunk(f32x4 v, int valid) {
-  f32x4 r;
-  r[0] = valid >= 4 ? v[0] : valid == 3 ? v[1] : valid == 2 ? v[2] : valid == 1 ? v[3] : 0.0f;
-  r[1] = valid >= 4 ? v[1] : valid == 3 ? v[2] : valid == 2 ? v[3] : 0.0f;
-  r[2] = valid >= 4 ? v[2] : valid == 3 ? v[3] : 0.0f;
-  r[3] = valid >= 4 ? v[3] : 0.0f;
-  return r;
+  const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+  float r0 = 0.0f, r1 = 0.0f, r2 = 0.0f, r3 = 0.0f;
+  r0 = valid == 1 ? v3 : r0;
+  r0 = valid == 2 ? v2 : r0;
+  r1 = valid == 2 ? v3 : r1;
+  r0 = valid == 3 ? v1 : r0;
+  r1 = valid == 3 ? v2 : r1;
+  r2 = valid == 3 ? v3 : r2;
+  r0 = valid >= 4 ? v0 : r0;
+  r1 = valid >= 4 ? v1 : r1;
+  r2 = valid >= 4 ? v2 : r2;
+  r3 = valid >= 4 ? v3 : r3;
+  return f32x4{r0, r1, r2, r3};
 }
 
 // f(std::integral_constant<int, i>{}) for i = 0 .. N-1, unrolled at compile time.
@@ -134,6 +143,34 @@ struct Slab {
       int col = line0 + 4 * (slot % CPL);
       col = col <= extent - 4 ? col : extent - 4;
       return X + (int64_t)(slot / CPL) * ld + col;
+    }
+  }
+  // Register staging without branches, for the hand-ordered loop (whole
+  // slabs; a line-contiguous operand's lines at least 4 values long). Chunk
+  // idx of the slab at k = 0 is read from chunk_src: k-contiguous lines past
+  // the extent repeat the last line, and a line-contiguous chunk that crosses
+  // the end of the lines is read as the line's last whole chunk, of which
+  // chunk_valid values belong to the chunk (4: all); store_chunk moves them
+  // into place. The LDS layout is that of store().
+  __device__ static const float* chunk_src(const float* X, int64_t ld, int line0, int extent, int idx) {
+    if constexpr (KCONTIG) {
+      int line = line0 + idx / CPL;
+      line = line < extent ? line : extent - 1;
+      return X + (int64_t)line * ld + 4 * (idx % CPL);
+    } else {
+      const int col = line0 + 4 * (idx % CPL);
+      return X + (int64_t)(idx / CPL) * ld + (col <= extent - 4 ? col : extent - 4);
+    }
+  }
+  __device__ static int chunk_valid(int line0, int extent, int idx) {
+    return KCONTIG ? 4 : extent - (line0 + 4 * (idx % CPL));
+  }
+  __device__ static void store_chunk(float* lds, f32x4 v, int valid, int idx) {
+    if constexpr (KCONTIG) {
+      const int line = idx / CPL;
+      *reinterpret_cast<f32x4*>(lds + line * BK + 4 * ((idx % CPL) ^ swz<BK>(line))) = v;
+    } else {
+      *reinterpret_cast<f32x4*>(lds + (idx / CPL) * ROWS + 4 * (idx % CPL)) = line_end_chunk(v, valid);
     }
   }
   // Offset of the slab at k0 from the slab at k = 0.
@@ -346,11 +383,11 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
 
   // ---- register staging (edge tiles, unaligned operands, the K tail) ------
   f32x4 ra[SA::CHUNKS], rb[SB::CHUNKS];
-  auto load_regs = [&](int k0, bool tail) {
+  auto load_regs = [&](int k0, bool tail) __attribute__((always_inline)) {
     SA::load(ra, A, g.lda, m0, M, K, k0, tail, t);
     SB::load(rb, B, g.ldb, n0, N, K, k0, tail, t);
   };
-  auto store_regs = [&](auto stage) {
+  auto store_regs = [&](auto stage) __attribute__((always_inline)) {
     SA::store(stage_a(stage), ra, m0, M, t);
     SB::store(stage_b(stage), rb, n0, N, t);
   };
@@ -370,7 +407,7 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto compute = [&](auto stage) {
+  auto compute = [&](auto stage) __attribute__((always_inline)) {
     const float* as = SA::frag_base(stage_a(stage), wm * Cfg::WTM, l32, h) + (SA::KC ? 0 : SA::k_offset(kbase, BM));
     const float* bs = SB::frag_base(stage_b(stage), wn * Cfg::WTN, l32, h) + (SB::KC ? 0 : SB::k_offset(kbase, BN));
 #pragma unroll
@@ -389,51 +426,98 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][u], bf[j][u], acc[i][j], 0, 0, 0);
     }
   };
+  // The same over a partial slab whose first r < KSUB values are all that is
+  // left (the rest zeroed): MFMA step u of fragment set kk multiplies
+  // k = kk + u and kk + 4 + u, so only the steps with kk + u < r run.
+  auto compute_partial = [&](auto stage, int r) __attribute__((always_inline)) {
+    const float* as = SA::frag_base(stage_a(stage), wm * Cfg::WTM, l32, h) + (SA::KC ? 0 : SA::k_offset(kbase, BM));
+    const float* bs = SB::frag_base(stage_b(stage), wn * Cfg::WTN, l32, h) + (SB::KC ? 0 : SB::k_offset(kbase, BN));
+#pragma unroll
+    for (int kk = 0; kk < Cfg::KSUB; kk += 8) {
+      if (kk < r) {
+        f32x4 af[FM], bf[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = SA::frag(as, i, kk, akey);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[j] = SB::frag(bs, j, kk, bkey);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (kk + u < r) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+              for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][u], bf[j][u], acc[i][j], 0, 0, 0);
+          }
+      }
+    }
+  };
 
   // ---- K loop ---------------------------------------------------------------
   const int nfull = K / BK;               // slabs with no k >= K
   const bool tail = (K % BK) != 0;
-  if constexpr (DIRECT) {
-    // STAGES-deep pipeline of direct loads over the full slabs: slab s+ST-1 is
-    // in flight while slab s is multiplied (slab s lives in stage s % ST).
-    // Each wave waits for its own loads of the next slab, then the barrier
-    // publishes them to the workgroup. The loop is unrolled by ST so every
-    // stage index is a constant.
-    // Each wave has per_slab direct loads in flight per slab; the wait
-    // before a barrier lets the loads of the slabs after the next one stay in
-    // flight (vmcnt takes an immediate, hence the cases).
-    constexpr int per_slab = SA::PER_WAVE + SB::PER_WAVE;
-    static_assert(Cfg::SCHED || (ST - 2) * per_slab <= 15, "vmcnt field");
-    auto wait_slabs_ahead = [&](int ahead) {  // until at most `ahead` later slabs are in flight
-      if (ST > 3 && ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * per_slab));
-      else if (ST > 2 && ahead >= 1) __builtin_amdgcn_s_waitcnt(0x0F70 | per_slab);
-      else wait_loads();
+  // Register staging through stages 0 and 1, last slab peeled.
+  auto register_loop = [&]() __attribute__((always_inline)) {
+    const int nk = nfull + (tail ? 1 : 0);
+    load_regs(0, tail && nk == 1);
+    store_regs(S0{});
+    __syncthreads();
+    auto rstep = [&](auto cur, int s) __attribute__((always_inline)) {
+      using Other = std::integral_constant<int, 1 - decltype(cur)::value>;
+      if (s + 1 < nk) load_regs((s + 1) * BK, tail && s + 2 == nk);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(cur);
+      if (s + 1 < nk) store_regs(Other{});
+      __syncthreads();
     };
-    if constexpr (Cfg::SCHED) {
-      // One wave per SIMD, so nothing else fills the matrix pipe while this
-      // wave waits: slab s is multiplied in G groups of FM x FN MFMAs, and
-      // between groups the wave issues the next slab's direct loads (spread
-      // over the first quarter of the slab: measured 0.7% faster than over
-      // the first half, and faster than two or all-at-once groups) and the
-      // next fragment set's LDS reads (double-buffered in registers). The barrier that
-      // publishes slab s+1 comes two groups before the end of slab s (its
-      // last LDS reads were issued earlier), and slab s+1's first fragments
-      // are read while those two groups run (four when a group is a single
-      // MFMA). sched_barrier keeps this order.
-      // With ST stages the loads go ST - 1 slabs ahead, into the stage slab
-      // s - 1 has just left, and the barrier waits only for slab s + 1. A
-      // load past the last slab reloads the last slab instead, so every wave
-      // issues the same loads in every step (the vmcnt waits count them) and
-      // the loop has no branch (a branch makes the compiler wait for every
-      // LDS read at the join); those loads complete before a barrier like any
-      // other. A wave with a single 32 x 32 block keeps two accumulator
-      // chains (even and odd k steps), so that no MFMA waits for the one
-      // before it; they are added after the loop.
+    int s = 0;
+    for (; s + 2 <= nk; s += 2) {
+      rstep(S0{}, s);
+      rstep(S1{}, s + 1);
+    }
+    if (s < nk) rstep(S0{}, s);
+  };
+  if constexpr (Cfg::SCHED) {
+    // One wave per SIMD, so nothing else fills the matrix pipe while this
+    // wave waits: slab s is multiplied in G groups of FM x FN MFMAs, and
+    // between groups the wave issues the loads of a later slab (spread over
+    // the first quarter of the slab: with direct loads measured 0.7% faster
+    // than over the first half, and faster than two or all-at-once groups)
+    // and the next fragment set's LDS reads (double-buffered in registers).
+    // The barrier that publishes slab s+1 comes two groups before the end of
+    // slab s (its last LDS reads were issued earlier), and slab s+1's first
+    // fragments are read while those two groups run (four when a group is a
+    // single MFMA). sched_barrier keeps this order.
+    // Direct loads (DIRECT): with ST stages the loads go ST - 1 slabs ahead,
+    // into the stage slab s - 1 has just left, and the barrier waits only for
+    // slab s + 1.
+    // Register staging (operands of any alignment): two LDS stages and one
+    // slab in registers. In step s the registers hold slab s + 1; each
+    // group that loads first writes its chunks of them to the stage slab
+    // s - 1 has left, then reloads them with slab s + 2 (the compiler waits
+    // for each chunk's load, issued a whole step before). The barrier
+    // publishes slab s + 1. A partial last slab follows the loop, staged on
+    // its own. It needs a whole slab and, for a line-contiguous operand,
+    // lines of at least 4 values (the whole-chunk reads of its last chunk);
+    // smaller problems take the plain register loop.
+    // In both, a load past the last slab reloads the last slab instead, so
+    // every wave issues the same loads in every step (the vmcnt waits count
+    // them) and the loop has no branch (a branch makes the compiler wait for
+    // every LDS read at the join); those loads complete before a barrier like
+    // any other. A wave with a single 32 x 32 block keeps two accumulator
+    // chains (even and odd k steps), so that no MFMA waits for the one
+    // before it; they are added after the loop.
+    const bool sched = DIRECT || (nfull >= 1 && (SA::KC || M >= 4) && (SB::KC || N >= 4));
+    if (sched) {
       static_assert(Cfg::KG == 1 && (BK / 8) % 2 == 0, "scheduled loop: no k groups, an even number of fragment sets");
-      constexpr int KK = BK / 8;                       // fragment sets per slab, 8 k each
-      constexpr int G = 4 * KK;                        // MFMA groups per slab
-      constexpr int NL = SA::PER_WAVE + SB::PER_WAVE;  // this wave's direct loads per slab
-      constexpr int LG = G / 4;                        // groups that issue them
+      constexpr int KK = BK / 8;                 // fragment sets per slab, 8 k each
+      constexpr int G = 4 * KK;                  // MFMA groups per slab
+      constexpr int SST = DIRECT ? ST : 2;       // LDS stages the loop cycles through
+      constexpr int AHEAD = DIRECT ? ST - 1 : 2;  // step s loads slab s + AHEAD
+      // per slab: this wave's direct loads, or this thread's register chunks
+      constexpr int NA = DIRECT ? SA::PER_WAVE : SA::CHUNKS;
+      constexpr int NL = NA + (DIRECT ? SB::PER_WAVE : SB::CHUNKS);
+      constexpr int LG = G / 4;                  // groups that issue them
       // The barrier group: after the slab's last LDS reads (issued in group
       // G - 7) and while the set the next slab's first reads go to is free
       // (from group G - 4 on); with one MFMA per group, four groups leave
@@ -460,30 +544,69 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
 #pragma unroll
         for (int j = 0; j < FN; ++j) bf[SET][j] = SB::frag(bs, j, kk, bkey);
       };
-      auto issue_one = [&](int q, int k0, auto stage) __attribute__((always_inline)) {
-        if (q < SA::PER_WAVE)
-          copy16_to_lds(a_src[q] + SA::k_offset(k0, g.lda), stage_a(stage) + (q * NW + wave) * 256);
+      // register staging: each chunk's source at k = 0 and its values inside the lines
+      constexpr int RA = DIRECT ? 1 : SA::CHUNKS, RB = DIRECT ? 1 : SB::CHUNKS;
+      const float* pa[RA];
+      const float* pb[RB];
+      int va[RA], vb[RB];
+      if constexpr (!DIRECT) {
+#pragma unroll
+        for (int c = 0; c < RA; ++c) {
+          pa[c] = SA::chunk_src(A, g.lda, m0, M, c * Cfg::NT + t);
+          va[c] = SA::chunk_valid(m0, M, c * Cfg::NT + t);
+        }
+#pragma unroll
+        for (int c = 0; c < RB; ++c) {
+          pb[c] = SB::chunk_src(B, g.ldb, n0, N, c * Cfg::NT + t);
+          vb[c] = SB::chunk_valid(n0, N, c * Cfg::NT + t);
+        }
+      }
+      // load q of the slab at k0: a direct load into `stage`, or chunk q into registers
+      auto load_one = [&](int q, int k0, auto stage) __attribute__((always_inline)) {
+        if constexpr (DIRECT) {
+          if (q < NA)
+            copy16_to_lds(a_src[q] + SA::k_offset(k0, g.lda), stage_a(stage) + (q * NW + wave) * 256);
+          else
+            copy16_to_lds(b_src[q - NA] + SB::k_offset(k0, g.ldb), stage_b(stage) + ((q - NA) * NW + wave) * 256);
+        } else {
+          if (q < NA)
+            ra[q] = load16(pa[q] + SA::k_offset(k0, g.lda));
+          else
+            rb[q - NA] = load16(pb[q - NA] + SB::k_offset(k0, g.ldb));
+        }
+      };
+      // register chunk q to `stage`
+      auto store_one = [&](int q, auto stage) __attribute__((always_inline)) {
+        if (q < NA)
+          SA::store_chunk(stage_a(stage), ra[q], va[q], q * Cfg::NT + t);
         else
-          copy16_to_lds(b_src[q - SA::PER_WAVE] + SB::k_offset(k0, g.ldb),
-                        stage_b(stage) + ((q - SA::PER_WAVE) * NW + wave) * 256);
+          SB::store_chunk(stage_b(stage), rb[q - NA], vb[q - NA], (q - NA) * Cfg::NT + t);
       };
       using Z = std::integral_constant<int, 0>;
       auto group = [&](auto cur, auto gi_c, int k1) __attribute__((always_inline)) {
         constexpr int gi = decltype(gi_c)::value;
         constexpr int kk = gi / 4, u = gi % 4, set = kk & 1;
         constexpr int CUR = decltype(cur)::value;
-        using Next = std::integral_constant<int, (CUR + ST - 1) % ST>;       // where slab s + ST - 1 goes
-        using Following = std::integral_constant<int, (CUR + 1) % ST>;       // where slab s + 1 is
+        using Next = std::integral_constant<int, (CUR + SST - 1) % SST>;   // where slab s + ST - 1 goes
+        using Following = std::integral_constant<int, (CUR + 1) % SST>;    // where slab s + 1 is
         // The next set is read one group into this one: the compiler waits for
         // every outstanding LDS read before the next group that uses a set, so
         // reads issued right before such a group would stall it.
         if constexpr (u == 1 && kk + 1 < KK) read_set(cur, std::integral_constant<int, (kk + 1) & 1>{}, (kk + 1) * 8);
         if constexpr (gi < LG) {
 #pragma unroll
-          for (int q = gi * PER_G; q < (gi + 1) * PER_G && q < NL; ++q) issue_one(q, k1, Next{});
+          for (int q = gi * PER_G; q < (gi + 1) * PER_G && q < NL; ++q) {
+            if constexpr (DIRECT) {
+              load_one(q, k1, Next{});
+            } else {  // the reload reuses the chunk's registers once the write has them
+              store_one(q, Following{});
+              __builtin_amdgcn_sched_barrier(0);
+              load_one(q, k1, Z{});
+            }
+          }
         }
         if constexpr (gi == BAR_G) {
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm((ST - 2) * NL));  // slab s + 1 has landed
+          if constexpr (DIRECT) __builtin_amdgcn_s_waitcnt(vmcnt_imm((ST - 2) * NL));  // slab s + 1 has landed
           __syncthreads();
           read_set(Following{}, Z{}, 0);
         }
@@ -500,32 +623,43 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
         __builtin_amdgcn_sched_barrier(0);
       };
       auto sched_step = [&](auto cur, int s) __attribute__((always_inline)) {
-        const int k1 = (s + ST - 1 < nfull ? s + ST - 1 : nfull - 1) * BK;
+        const int k1 = (s + AHEAD < nfull ? s + AHEAD : nfull - 1) * BK;
         static_for<G>([&](auto gi_c) __attribute__((always_inline)) { group(cur, gi_c, k1); });
       };
-      static_assert((ST - 2) * NL < 64, "vmcnt field");
-      // slabs 0 .. ST-2 (a slab past the last reloads the last one)
-      static_for<ST - 1>([&](auto i_c) __attribute__((always_inline)) {
-        constexpr int i = decltype(i_c)::value;
-        const int k0 = (i < nfull ? i : nfull - 1) * BK;
+      static_assert(!DIRECT || (ST - 2) * NL < 64, "vmcnt field");
+      if constexpr (DIRECT) {
+        // slabs 0 .. ST-2 (a slab past the last reloads the last one)
+        static_for<ST - 1>([&](auto i_c) __attribute__((always_inline)) {
+          constexpr int i = decltype(i_c)::value;
+          const int k0 = (i < nfull ? i : nfull - 1) * BK;
 #pragma unroll
-        for (int q = 0; q < NL; ++q) issue_one(q, k0, std::integral_constant<int, i>{});
-      });
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((ST - 2) * NL));  // slab 0 has landed
+          for (int q = 0; q < NL; ++q) load_one(q, k0, std::integral_constant<int, i>{});
+        });
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((ST - 2) * NL));  // slab 0 has landed
+      } else {
+        // slab 0 to stage 0, slab 1 into the registers
+#pragma unroll
+        for (int q = 0; q < NL; ++q) load_one(q, 0, Z{});
+#pragma unroll
+        for (int q = 0; q < NL; ++q) store_one(q, S0{});
+        const int k1 = (nfull > 1 ? 1 : 0) * BK;
+#pragma unroll
+        for (int q = 0; q < NL; ++q) load_one(q, k1, Z{});
+      }
       __syncthreads();
       read_set(S0{}, Z{}, 0);
       int s = 0;
-      for (; s + ST <= nfull; s += ST) {
+      for (; s + SST <= nfull; s += SST) {
         sched_step(S0{}, s);
         sched_step(S1{}, s + 1);
-        if constexpr (ST > 2) sched_step(S2{}, s + 2);
-        if constexpr (ST > 3) sched_step(S3{}, s + 3);
+        if constexpr (SST > 2) sched_step(S2{}, s + 2);
+        if constexpr (SST > 3) sched_step(S3{}, s + 3);
       }
       if (s < nfull) sched_step(S0{}, s);
-      if constexpr (ST > 2) {
+      if constexpr (SST > 2) {
         if (s + 1 < nfull) sched_step(S1{}, s + 1);
       }
-      if constexpr (ST > 3) {
+      if constexpr (SST > 3) {
         if (s + 2 < nfull) sched_step(S2{}, s + 2);
       }
       if constexpr (NACC == 2) {
@@ -534,7 +668,40 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
 #pragma unroll
           for (int j = 0; j < FN; ++j) acc[i][j] += acc2[i][j];
       }
+      // With more than two stages the last step's reloads may still be in
+      // flight past its barrier: they land before the stage arrays are reused
+      // or the wave ends.
+      if constexpr (DIRECT && ST > 2) wait_loads();
+      // A partial last slab (k >= K zeroed), staged through registers after
+      // every wave has left the stage arrays.
+      if constexpr (KTAIL || !DIRECT) {
+        if (tail) {
+          load_regs(nfull * BK, true);
+          __syncthreads();
+          store_regs(S0{});
+          __syncthreads();
+          compute_partial(S0{}, K - nfull * BK);
+        }
+      }
     } else {
+      register_loop();
+    }
+  } else if constexpr (DIRECT) {
+    // STAGES-deep pipeline of direct loads over the full slabs: slab s+ST-1 is
+    // in flight while slab s is multiplied (slab s lives in stage s % ST).
+    // Each wave waits for its own loads of the next slab, then the barrier
+    // publishes them to the workgroup. The loop is unrolled by ST so every
+    // stage index is a constant.
+    // Each wave has per_slab direct loads in flight per slab; the wait
+    // before a barrier lets the loads of the slabs after the next one stay in
+    // flight (vmcnt takes an immediate, hence the cases).
+    constexpr int per_slab = SA::PER_WAVE + SB::PER_WAVE;
+    static_assert((ST - 2) * per_slab <= 15, "vmcnt field");
+    auto wait_slabs_ahead = [&](int ahead) {  // until at most `ahead` later slabs are in flight
+      if (ST > 3 && ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * per_slab));
+      else if (ST > 2 && ahead >= 1) __builtin_amdgcn_s_waitcnt(0x0F70 | per_slab);
+      else wait_loads();
+    };
     issue_direct(0, S0{});
     if (ST > 2 && nfull > 1) issue_direct(BK, S1{});
     if (ST > 3 && nfull > 2) issue_direct(2 * BK, S2{});
@@ -566,7 +733,6 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
     if constexpr (ST > 3) {
       if (s + 2 < nfull) step(S2{}, s + 2);
     }
-    }
     if constexpr (KTAIL) {
       if (tail) {
         load_regs(nfull * BK, true);
@@ -577,25 +743,7 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
       }
     }
   } else {
-    // Register staging through stages 0 and 1, last slab peeled.
-    const int nk = nfull + (tail ? 1 : 0);
-    load_regs(0, tail && nk == 1);
-    store_regs(S0{});
-    __syncthreads();
-    auto rstep = [&](auto cur, int s) {
-      using Other = std::integral_constant<int, 1 - decltype(cur)::value>;
-      if (s + 1 < nk) load_regs((s + 1) * BK, tail && s + 2 == nk);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(cur);
-      if (s + 1 < nk) store_regs(Other{});
-      __syncthreads();
-    };
-    int s = 0;
-    for (; s + 2 <= nk; s += 2) {
-      rstep(S0{}, s);
-      rstep(S1{}, s + 1);
-    }
-    if (s < nk) rstep(S0{}, s);
+    register_loop();
   }
 
   // ---- k groups: add the groups' sums in ascending group order ----------
@@ -1103,6 +1251,16 @@ hipError_t launch_mfma_dma(const GemmArgs& g, hipStream_t stream) {
   return hipLaunchKernel(kernel, dim3((unsigned)tiles, (unsigned)g.batch), dim3(Cfg::NT), args, 0, stream);
 }
 
+// The hand-ordered loop staged through registers: operands of any alignment.
+template <class Cfg>
+hipError_t launch_mfma_rs(const GemmArgs& g, hipStream_t stream) {
+  const int64_t tiles = (int64_t)((g.M + Cfg::BM - 1) / Cfg::BM) * ((g.N + Cfg::BN - 1) / Cfg::BN);
+  GemmArgs a = g;
+  void* args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&mfma_dma_kernel<Cfg, false>),
+                         dim3((unsigned)tiles, (unsigned)g.batch), dim3(Cfg::NT), args, 0, stream);
+}
+
 template <class Cfg>
 hipError_t launch_mfma_dma_streamk(const GemmArgs& g, const StreamKPlan& plan, int grid, bool direct,
                                    hipStream_t stream) {
@@ -1161,6 +1319,14 @@ hipError_t launch_mfma_dma_streamk(const GemmArgs& g, const StreamKPlan& plan, i
   SGEMM_MFMA_DMA_SCHED_CFG(BM, BN, BK, WM, WN, 1, 0, "_tn"),          \
       SGEMM_MFMA_DMA_SCHED_CFG(BM, BN, BK, WM, WN, 0, 1, "_nt"),      \
       SGEMM_MFMA_DMA_SCHED_CFG(BM, BN, BK, WM, WN, 1, 1, "_tt")
+// The hand-ordered loop staged through registers (_rs): no direct loads, so
+// operands of any alignment; every slab and the K tail through registers.
+#define SGEMM_MFMA_RS_SCHED_CFG(BM, BN, BK, WM, WN, TA, TB, SFX)                                               \
+  {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_rs_sched" SFX, KIND_MFMA, BM, BN, BK, 64 * WM * WN, TA, TB,    \
+   &launch_mfma_rs<DmaSchedCfg<BM, BN, BK, WM, WN, TA, TB>>,                                                     \
+   reinterpret_cast<const void*>(&mfma_dma_kernel<DmaSchedCfg<BM, BN, BK, WM, WN, TA, TB>, false>), 1, nullptr,   \
+   {nullptr, nullptr}, 1}
+#define SGEMM_MFMA_RS_SCHED(BM, BN, BK, WM, WN) SGEMM_MFMA_RS_SCHED_CFG(BM, BN, BK, WM, WN, 0, 0, "")
 // The same with a stream-K form (configurations without k groups).
 #define SGEMM_MFMA_DMA_SK_CFG(BM, BN, BK, WM, WN, ST, TA, TB, SFX)                                         \
   {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SFX, KIND_MFMA, BM, BN, BK, 64 * WM * WN, TA, TB,        \
@@ -1209,6 +1375,10 @@ KernelConfig kMfmaDmaConfigs[] = {
     SGEMM_MFMA_DMA_SCHED_ST_OPS(64, 64, 32, 2, 2, 4),
     SGEMM_MFMA_DMA_SCHED_ST(64, 64, 64, 2, 2, 3),
     SGEMM_MFMA_DMA_SCHED_ST_OPS(64, 64, 64, 2, 2, 3),
+    SGEMM_MFMA_DMA_SCHED_ST(192, 128, 32, 2, 2, 2),
+    SGEMM_MFMA_DMA_SCHED_ST(192, 128, 32, 2, 2, 3),
+    // hand-ordered tiles staged through registers: any alignment
+    SGEMM_MFMA_RS_SCHED(192, 128, 32, 2, 2),
 };
 const int kNumMfmaDmaConfigs = sizeof(kMfmaDmaConfigs) / sizeof(kMfmaDmaConfigs[0]);
 

@@ -172,7 +172,10 @@ struct Resolved {
   ResolvedBlock block[2][2];
 };
 
-bool is_direct_config(int id) { return id >= kNumMfmaConfigs && id < kNumMfmaConfigs + kNumMfmaDmaConfigs; }
+bool is_direct_config(int id) {
+  return id >= kNumMfmaConfigs && id < kNumMfmaConfigs + kNumMfmaDmaConfigs &&
+         !kMfmaDmaConfigs[id - kNumMfmaConfigs].staged;
+}
 
 // Fill model of a launch of configuration c on an M x N x K problem (batch
 // entries in grid.y): workgroups are dealt round-robin over the XCDs and

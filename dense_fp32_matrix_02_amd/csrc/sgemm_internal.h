@@ -65,6 +65,10 @@ struct KernelConfig {
   // staged through registers [0] and by direct loads [1] (occupancy queries).
   StreamKLaunchFn streamk;
   const void* streamk_kernel[2];
+  // 1: a configuration of the direct-load kernel family that stages every slab
+  // through registers (the hand-ordered tiles named _rs), so it has no direct
+  // path and takes operands of any alignment.
+  int staged;
 };
 
 // Host-only tables (not const: a const global would also be emitted for the

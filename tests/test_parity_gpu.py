@@ -308,7 +308,7 @@ def test_very_long_k_exact(kind):
         np.testing.assert_array_equal(Cs.cpu().numpy(), want)
 
 
-DIRECT_IDS = [i for i, n in enumerate(CONFIG_NAMES) if "_lds" in n or n.endswith("_sched")]
+DIRECT_IDS = [i for i, n in enumerate(CONFIG_NAMES) if "_lds" in n]
 
 
 SCHED_IDS = [i for i, n in enumerate(CONFIG_NAMES) if n.endswith("_sched")]
@@ -324,7 +324,8 @@ def test_hand_ordered_loop_repeats_bitwise(cid):
     M, N, K = 1100, 1020, 2048
     A, B = workloads.draw(M, N, K, 31, "uniform")
     Ad, Bd = G.dev(A), G.dev(B)
-    assert sg.sgemm_mi355_config_staging(cid, M, N, K, Ad.data_ptr(), K, Bd.data_ptr(), N) == 1
+    direct = 1 if "_lds" in CONFIG_NAMES[cid] else 0  # _rs: staged through registers
+    assert sg.sgemm_mi355_config_staging(cid, M, N, K, Ad.data_ptr(), K, Bd.data_ptr(), N) == direct
     print(f"[gpu] repeated runs config={CONFIG_NAMES[cid]} M={M} N={N} K={K}", flush=True)
     first = sg.gemm(Ad, Bd, config=cid)
     for _ in range(10):
@@ -401,6 +402,53 @@ def test_direct_lds_configs_exact(cid):
     Cs = sg.gemm_splitk(G.dev(_stored(A, opA)), G.dev(_stored(B, opB)), splits=3, opA=opA, opB=opB, config=cid)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(Cs.cpu().numpy(), oracle.sgemm_f32(np_(A), np_(B)))
+
+
+RS_IDS = [i for i, n in enumerate(CONFIG_NAMES) if "_rs_sched" in n]
+
+
+@pytest.mark.parametrize("cid", RS_IDS, ids=[CONFIG_NAMES[i] for i in RS_IDS])
+def test_register_staged_hand_ordered_any_alignment(cid):
+    """The hand-ordered loop staged through registers takes bases at any
+    4-byte offset, odd leading dimensions and extents that are not multiples
+    of 4: lines past the edge of C repeat the last line, a chunk that crosses
+    the end of B's rows is read as the row's last whole chunk and moved into
+    place, a K that is not a whole number of slabs ends in a slab staged on
+    its own, and problems under one slab deep, or with fewer than 4 columns,
+    take the plain register loop. Exact on integer inputs, with NaN around
+    every operand and in C's padding, which must stay."""
+    bm, bn, bk, _ = sg.sgemm_mi355_config_info(cid)
+    cases = [  # M, N, K, lda pad, ldb pad, ldc pad, A offset, B offset, C offset (floats)
+        (bm + 1, bn - 3, 4 * bk, 1, 3, 1, 1, 2, 3),
+        (2 * bm + 5, 2 * bn + 7, 9 * bk + 3, 0, 0, 0, 3, 1, 1),
+        (1, 1, bk, 0, 0, 0, 1, 1, 1),
+        (3, bn + 1, 5 * bk + 1, 2, 1, 2, 2, 3, 0),
+        (bm - 1, 2, 2 * bk + 31, 1, 0, 1, 0, 1, 2),
+        (bm + 7, 5, 3 * bk, 3, 2, 0, 1, 3, 1),
+        (2 * bm, 2 * bn, bk - 1, 1, 1, 1, 2, 1, 3),
+        (3001 % bm + bm, 2047 % bn + bn, 1537, 0, 0, 0, 0, 0, 0),
+    ]
+    for seed, (M, N, K, pa, pb, pc, oa, ob, oc) in enumerate(cases, start=2500):
+        A, B = workloads.draw(M, N, K, seed, "int4")
+        lda, ldb, ldc = K + pa, N + pb, N + pc
+        abuf = torch.full((oa + M * lda + 5,), float("nan"), device="cuda")
+        bbuf = torch.full((ob + K * ldb + 5,), float("nan"), device="cuda")
+        cbuf = torch.full((oc + M * ldc + 5,), float("nan"), device="cuda")
+        Av = abuf[oa:oa + M * lda].view(M, lda)
+        Bv = bbuf[ob:ob + K * ldb].view(K, ldb)
+        Cv = cbuf[oc:oc + M * ldc].view(M, ldc)
+        Av[:, :K] = G.dev(A)
+        Bv[:, :N] = G.dev(B)
+        assert sg.sgemm_mi355_config_staging(cid, M, N, K, Av.data_ptr(), lda, Bv.data_ptr(), ldb) == 0
+        print(f"[gpu] config={CONFIG_NAMES[cid]} M={M} N={N} K={K} lda={lda} ldb={ldb} "
+              f"offsets={oa},{ob},{oc}", flush=True)
+        rc = sg.sgemm_mi355_with_config(M, N, K, Av.data_ptr(), lda, Bv.data_ptr(), ldb, Cv.data_ptr(), ldc,
+                                        torch.cuda.current_stream().cuda_stream, cid)
+        assert rc == sg.OK
+        torch.cuda.synchronize()
+        G.check_exact(np.ascontiguousarray(Cv[:, :N].cpu().numpy()), np_(A), np_(B))
+        assert np.isnan(Cv[:, N:].cpu().numpy()).all()
+        assert np.isnan(cbuf[:oc].cpu().numpy()).all() and np.isnan(cbuf[oc + M * ldc:].cpu().numpy()).all()
 
 
 @pytest.mark.parametrize("cid", DIRECT_IDS, ids=[CONFIG_NAMES[i] for i in DIRECT_IDS])
