@@ -24,6 +24,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -48,7 +49,7 @@ def kernel_sources(config_name: str):
     """The source files that define a configuration's kernel."""
     if config_name.startswith("valu"):
         return ("kernels_valu.hip", "sgemm_internal.h")
-    if "_lds" in config_name or "_rs_sched" in config_name:
+    if "_lds" in config_name or re.search(r"_rs\d*_sched", config_name):
         return ("kernels_mfma_dma.hip", "sgemm_internal.h")
     return ("kernels_mfma.hip", "sgemm_internal.h")
 

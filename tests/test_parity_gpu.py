@@ -13,6 +13,7 @@ result for the integer variant.
 """
 from __future__ import annotations
 
+import re
 import numpy as np
 import pytest
 import torch
@@ -404,7 +405,7 @@ def test_direct_lds_configs_exact(cid):
     np.testing.assert_array_equal(Cs.cpu().numpy(), oracle.sgemm_f32(np_(A), np_(B)))
 
 
-RS_IDS = [i for i, n in enumerate(CONFIG_NAMES) if "_rs_sched" in n]
+RS_IDS = [i for i, n in enumerate(CONFIG_NAMES) if re.search(r"_rs\d*_sched", n)]
 
 
 @pytest.mark.parametrize("cid", RS_IDS, ids=[CONFIG_NAMES[i] for i in RS_IDS])
