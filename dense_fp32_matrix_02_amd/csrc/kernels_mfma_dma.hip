@@ -787,12 +787,51 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
     }
   }
 
-  // ---- epilogue: masked stores; C is read only when beta != 0 ------------
+  // ---- epilogue: C is read only when beta != 0 ----------------------------
+  // Element r of block (i, j) belongs to row row0 + 32 i + 8 (r / 4) + r % 4
+  // and column col0 + 32 j. A tile wholly inside C stores without masks: the
+  // wave's first row and column give a uniform base, each element adds a
+  // uniform offset, and a lane adds its own (its row within four and its
+  // column), the same for every element and 32-bit while 4 ldc is; with
+  // beta != 0 a block's 16 values of C are all read before any is written.
+  // Edge tiles mask every element.
   float* C = g.C + (int64_t)blockIdx.y * g.strideC;
   const int row0 = m0 + wm * Cfg::WTM + 4 * h;
   const int col0 = n0 + wn * Cfg::WTN + l32;
   const float alpha = g.alpha, beta = g.beta;
-  auto store_tile = [&](auto op) {
+  if (m0 + BM <= M && n0 + BN <= N && g.ldc < (1 << 27)) {
+    float* cw = C + (int64_t)(m0 + wm * Cfg::WTM) * g.ldc + (n0 + wn * Cfg::WTN);
+    const uint32_t lane_off = (uint32_t)(4 * h) * (uint32_t)g.ldc + (uint32_t)l32;
+    auto at = [&](int i, int j, int r) __attribute__((always_inline)) -> float* {
+      return cw + ((int64_t)(32 * i + 8 * (r >> 2) + (r & 3)) * g.ldc + 32 * j) + lane_off;
+    };
+    auto each = [&](auto op) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) op(at(i, j, r), acc[i][j][r]);
+    };
+    if (alpha == 1.0f && beta == 0.0f) {
+      each([](float* p, float v) { *p = v; });
+    } else if (beta == 0.0f) {
+      each([alpha](float* p, float v) { *p = alpha * v; });
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          float old[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) old[r] = *at(i, j, r);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) *at(i, j, r) = __builtin_fmaf(beta, old[r], alpha * acc[i][j][r]);
+        }
+    }
+    return;
+  }
+  auto store_tile = [&](auto op) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
