@@ -4,9 +4,10 @@ shape and emit the tile table the library compiles in.
 The best tile is found by measurement, not derived (CUDA Handbook section
 17.3 sweeps the microtile; GPU Parallel Book ch. 9, section 9.6 sweeps the
 occupancy setting). For each shape every matrix-core configuration built for
-the op pair runs on seeded U[-1,1) inputs; the median of `reps` event-timed
-launches is recorded, with each configuration's occupancy (workgroups per
-compute unit, from the HIP runtime).
+the op pair runs on seeded U[-1,1) inputs; the time per launch of `reps`
+launches run back to back (as bench.py times them) is recorded, with each
+configuration's occupancy (workgroups per compute unit, from the HIP
+runtime).
 
     python -m dense_fp32_matrix_02_amd.tune [--shapes 8192x8192x8192,...]
         [--grid | --smallk-grid] [--reps 20] [--json results.json] [--table tile_table.inc]
@@ -50,7 +51,7 @@ TABLE_HEADER = """\
 // that misaligned problems have register-staged candidates) with their
 // occupancy (workgroups one compute unit holds, from the HIP runtime), then
 // per shape {{M, N, K}} and the
-// candidates' median times in microseconds; 0 marks a time more than
+// candidates' times per launch in microseconds; 0 marks a time more than
 // {cut}x the shape's best (never a candidate there). Then every
 // configuration of the op pair with its occupancy and its median time per
 // unit of modelled busy time over the shapes: the selection's estimate for
@@ -61,8 +62,8 @@ TABLE_HEADER = """\
 // per shape of a second grid, the fastest split count of sgemm_mi355_splitk,
 // which sgemm_mi355_select_splitk suggests for shapes near it.
 //
-// Written by dense_fp32_matrix_02_amd/tune.py (median of {reps} launches per
-// configuration and shape{passes}).
+// Written by dense_fp32_matrix_02_amd/tune.py (time per launch of {reps}
+// launches run back to back, per configuration and shape{passes}).
 """
 
 # Times more than this factor above a shape's best are stored as 0 (not a
@@ -95,9 +96,9 @@ GRID_SIDES = (128, 256, 512, 1024, 2048, 4096, 8192)
 GRID_KS = (256, 1024, 4096, 16384)
 # The short-K grid: products whose K is a few slabs, where the launch and the
 # store of C take much of the time. Their launches last microseconds, so they
-# are timed with more repetitions than the default, in two passes: a slow
-# spell of a tenth of a millisecond moves the median of 30 launches of 7 us
-# (one configuration measured 14 us in one row, 7 at its neighbours).
+# are timed with more repetitions than the default, in two passes (a slow
+# spell of a tenth of a millisecond once doubled one configuration's time in
+# one row, 14 us against 7 at its neighbours).
 SMALLK_KS = (32, 96)
 SMALLK_REPS = 30
 SMALLK_WARMUP = 10
@@ -126,20 +127,50 @@ def parse_shapes(text):
     return out
 
 
+_SLEEP_CYCLES_PER_US = None
+# Host time to issue one call, covered by the spin kernel queued ahead of the
+# timed calls (a ctypes call and a HIP enqueue take tens of microseconds).
+_ISSUE_US = 80.0
+
+
+def _queue_ahead(stream, us):
+    """Enqueue a spin kernel of about `us` microseconds on `stream`, so the
+    calls issued after it wait on the GPU and then run back to back."""
+    import torch
+
+    global _SLEEP_CYCLES_PER_US
+    if _SLEEP_CYCLES_PER_US is None:
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        s.record()
+        torch.cuda._sleep(1_000_000)
+        e.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_US = 1_000_000 / max(s.elapsed_time(e) * 1e3, 1.0)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(_SLEEP_CYCLES_PER_US * us))
+
+
 def time_call(call, reps, warmup):
-    """Median of `reps` event-timed calls after `warmup` untimed ones (ms)."""
+    """Time per call (ms) of `reps` calls run back to back between one pair of
+    events, after `warmup` untimed ones: the calls are queued behind a spin
+    kernel, so the host's issue cost stays out. This is how bench.py times a
+    workload; an event pair around each call adds a few microseconds per
+    call, more for some kernels than for others."""
     import torch
 
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         call(stream)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for s, e in ev:
-        s.record(stream)
-        call(stream)
-        e.record(stream)
     torch.cuda.synchronize()
-    return statistics.median(s.elapsed_time(e) for s, e in ev)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    _queue_ahead(stream, _ISSUE_US * reps)
+    s.record(stream)
+    for _ in range(reps):
+        call(stream)
+    e.record(stream)
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
 
 
 def make_inputs(M, N, K, opA, opB, batch):
@@ -188,7 +219,7 @@ def main(argv=None):
                          "(launches of a few microseconds)")
     ap.add_argument("--reps", type=int, default=20)
     ap.add_argument("--passes", type=int, default=1,
-                    help="time each shape's configurations this many times over, keeping each one's least median")
+                    help="time each shape's configurations this many times over, keeping each one's least time")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--kinds", default="mfma", help="mfma, valu or mfma,valu")
     ap.add_argument("--splitk", default="", help="split counts to time with sgemm_mi355_splitk, e.g. 2,4,8")

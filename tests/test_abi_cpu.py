@@ -764,7 +764,8 @@ def test_tuner_writes_the_table_it_documents(tmp_path):
     path = tmp_path / "table.inc"
     tune.write_table(rows, str(path), reps=5)
     # rows without a recorded repetition count take the argument's
-    assert "median of 5 to 30 launches per\n// configuration and shape, the least over up to 2 passes)" in path.read_text()
+    assert ("time per launch of 5 to 30\n// launches run back to back, per configuration and shape, the least over "
+            "up to 2 passes)") in path.read_text()
     blocks = _table(str(path))
     cands, shapes, times = blocks[(0, 0)]
     assert [n for n, _ in cands] == [big, mid]  # winners, in first-win order
