@@ -1414,6 +1414,10 @@ KernelConfig kMfmaDmaConfigs[] = {
     SGEMM_MFMA_DMA_SCHED_ST_OPS(64, 64, 32, 2, 2, 4),
     SGEMM_MFMA_DMA_SCHED_ST(64, 64, 64, 2, 2, 3),
     SGEMM_MFMA_DMA_SCHED_ST_OPS(64, 64, 64, 2, 2, 3),
+    // 128x128 tiles of four 64x64 waves: mid-size products (2048^3: 256 tiles)
+    SGEMM_MFMA_DMA_SCHED_ST(128, 128, 32, 2, 2, 4),
+    SGEMM_MFMA_DMA_SCHED_ST(128, 128, 64, 2, 2, 2),
+    SGEMM_MFMA_DMA_SCHED_ST_OPS(128, 128, 64, 2, 2, 2),
     SGEMM_MFMA_DMA_SCHED_ST(192, 128, 32, 2, 2, 2),
     SGEMM_MFMA_DMA_SCHED_ST(192, 128, 32, 2, 2, 3),
     // hand-ordered tiles staged through registers: any alignment
