@@ -1418,6 +1418,8 @@ KernelConfig kMfmaDmaConfigs[] = {
     SGEMM_MFMA_DMA_SCHED_ST(128, 128, 32, 2, 2, 4),
     SGEMM_MFMA_DMA_SCHED_ST(128, 128, 64, 2, 2, 2),
     SGEMM_MFMA_DMA_SCHED_ST_OPS(128, 128, 64, 2, 2, 2),
+    // 256x128 tiles of four 128x64 waves
+    SGEMM_MFMA_DMA_SCHED_ST(256, 128, 32, 2, 2, 2),
     SGEMM_MFMA_DMA_SCHED_ST(192, 128, 32, 2, 2, 2),
     SGEMM_MFMA_DMA_SCHED_ST(192, 128, 32, 2, 2, 3),
     // hand-ordered tiles staged through registers: any alignment
