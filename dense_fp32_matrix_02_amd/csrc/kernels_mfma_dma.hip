@@ -1366,6 +1366,10 @@ hipError_t launch_mfma_dma_streamk(const GemmArgs& g, const StreamKPlan& plan, i
    reinterpret_cast<const void*>(&mfma_dma_kernel<DmaSchedCfg<BM, BN, BK, WM, WN, TA, TB>, false>), 1, nullptr,   \
    {nullptr, nullptr}, 1}
 #define SGEMM_MFMA_RS_SCHED(BM, BN, BK, WM, WN) SGEMM_MFMA_RS_SCHED_CFG(BM, BN, BK, WM, WN, 0, 0, "")
+#define SGEMM_MFMA_RS_SCHED_OPS(BM, BN, BK, WM, WN)                  \
+  SGEMM_MFMA_RS_SCHED_CFG(BM, BN, BK, WM, WN, 1, 0, "_tn"),          \
+      SGEMM_MFMA_RS_SCHED_CFG(BM, BN, BK, WM, WN, 0, 1, "_nt"),      \
+      SGEMM_MFMA_RS_SCHED_CFG(BM, BN, BK, WM, WN, 1, 1, "_tt")
 // The same with a stream-K form (configurations without k groups).
 #define SGEMM_MFMA_DMA_SK_CFG(BM, BN, BK, WM, WN, ST, TA, TB, SFX)                                         \
   {"mfma32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SFX, KIND_MFMA, BM, BN, BK, 64 * WM * WN, TA, TB,        \
@@ -1424,6 +1428,7 @@ KernelConfig kMfmaDmaConfigs[] = {
     SGEMM_MFMA_DMA_SCHED_ST(192, 128, 32, 2, 2, 3),
     // hand-ordered tiles staged through registers: any alignment
     SGEMM_MFMA_RS_SCHED(192, 128, 32, 2, 2),
+    SGEMM_MFMA_RS_SCHED_OPS(192, 128, 32, 2, 2),
 };
 const int kNumMfmaDmaConfigs = sizeof(kMfmaDmaConfigs) / sizeof(kMfmaDmaConfigs[0]);
 

@@ -412,13 +412,16 @@ RS_IDS = [i for i, n in enumerate(CONFIG_NAMES) if re.search(r"_rs\d*_sched", n)
 def test_register_staged_hand_ordered_any_alignment(cid):
     """The hand-ordered loop staged through registers takes bases at any
     4-byte offset, odd leading dimensions and extents that are not multiples
-    of 4: lines past the edge of C repeat the last line, a chunk that crosses
-    the end of B's rows is read as the row's last whole chunk and moved into
-    place, a K that is not a whole number of slabs ends in a slab staged on
-    its own, and problems under one slab deep, or with fewer than 4 columns,
-    take the plain register loop. Exact on integer inputs, with NaN around
-    every operand and in C's padding, which must stay."""
+    of 4, in the operand layouts the configuration reads: lines past the edge
+    of C repeat the last line, a chunk that crosses the end of a
+    line-contiguous operand's lines is read as the line's last whole chunk and
+    moved into place, a K that is not a whole number of slabs ends in a slab
+    staged on its own, and problems under one slab deep, or with fewer than 4
+    lines where the lines are contiguous, take the plain register loop. Exact
+    on integer inputs, with NaN around every operand and in C's padding,
+    which must stay."""
     bm, bn, bk, _ = sg.sgemm_mi355_config_info(cid)
+    opA, opB = sg.sgemm_mi355_config_ops(cid)
     cases = [  # M, N, K, lda pad, ldb pad, ldc pad, A offset, B offset, C offset (floats)
         (bm + 1, bn - 3, 4 * bk, 1, 3, 1, 1, 2, 3),
         (2 * bm + 5, 2 * bn + 7, 9 * bk + 3, 0, 0, 0, 3, 1, 1),
@@ -431,20 +434,24 @@ def test_register_staged_hand_ordered_any_alignment(cid):
     ]
     for seed, (M, N, K, pa, pb, pc, oa, ob, oc) in enumerate(cases, start=2500):
         A, B = workloads.draw(M, N, K, seed, "int4")
-        lda, ldb, ldc = K + pa, N + pb, N + pc
-        abuf = torch.full((oa + M * lda + 5,), float("nan"), device="cuda")
-        bbuf = torch.full((ob + K * ldb + 5,), float("nan"), device="cuda")
+        As, Bs = _stored(A, opA), _stored(B, opB)
+        ra, ca = As.shape
+        rb, cb = Bs.shape
+        lda, ldb, ldc = ca + pa, cb + pb, N + pc
+        abuf = torch.full((oa + ra * lda + 5,), float("nan"), device="cuda")
+        bbuf = torch.full((ob + rb * ldb + 5,), float("nan"), device="cuda")
         cbuf = torch.full((oc + M * ldc + 5,), float("nan"), device="cuda")
-        Av = abuf[oa:oa + M * lda].view(M, lda)
-        Bv = bbuf[ob:ob + K * ldb].view(K, ldb)
+        Av = abuf[oa:oa + ra * lda].view(ra, lda)
+        Bv = bbuf[ob:ob + rb * ldb].view(rb, ldb)
         Cv = cbuf[oc:oc + M * ldc].view(M, ldc)
-        Av[:, :K] = G.dev(A)
-        Bv[:, :N] = G.dev(B)
+        Av[:, :ca] = G.dev(As)
+        Bv[:, :cb] = G.dev(Bs)
         assert sg.sgemm_mi355_config_staging(cid, M, N, K, Av.data_ptr(), lda, Bv.data_ptr(), ldb) == 0
         print(f"[gpu] config={CONFIG_NAMES[cid]} M={M} N={N} K={K} lda={lda} ldb={ldb} "
               f"offsets={oa},{ob},{oc}", flush=True)
-        rc = sg.sgemm_mi355_with_config(M, N, K, Av.data_ptr(), lda, Bv.data_ptr(), ldb, Cv.data_ptr(), ldc,
-                                        torch.cuda.current_stream().cuda_stream, cid)
+        rc = sg.sgemm_mi355_strided_batched_with_config(
+            opA, opB, M, N, K, 1.0, Av.data_ptr(), lda, 0, Bv.data_ptr(), ldb, 0, 0.0, Cv.data_ptr(), ldc, 0, 1,
+            torch.cuda.current_stream().cuda_stream, cid)
         assert rc == sg.OK
         torch.cuda.synchronize()
         G.check_exact(np.ascontiguousarray(Cv[:, :N].cpu().numpy()), np_(A), np_(B))
