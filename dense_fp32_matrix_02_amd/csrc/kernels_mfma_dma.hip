@@ -146,12 +146,18 @@ struct Slab {
     }
   }
   // Register staging without branches, for the hand-ordered loop (whole
-  // slabs; a line-contiguous operand's lines at least 4 values long). Chunk
-  // idx of the slab at k = 0 is read from chunk_src: k-contiguous lines past
-  // the extent repeat the last line, and a line-contiguous chunk that crosses
-  // the end of the lines is read as the line's last whole chunk, of which
-  // chunk_valid values belong to the chunk (4: all); store_chunk moves them
-  // into place. The LDS layout is that of store().
+  // slabs; a line-contiguous operand's lines at least 4 values long, and a
+  // tile that reaches past their end holding at least 4 of them). Chunk idx
+  // of the slab at k = 0 is read from chunk_src: k-contiguous lines past the
+  // extent repeat the last line, and a line-contiguous chunk that crosses the
+  // end of the lines is read as the line's last whole chunk, which ends where
+  // the lines end. store_chunk writes it chunk_shift floats before its slot,
+  // so each value lands on its own line; the values it writes over, at the
+  // end of the previous chunk's slot, are the same ones, and the slot's own
+  // last chunk_shift floats (lines past the extent, which feed only outputs
+  // that are never stored) keep what they held. Two 64-bit writes of 4-byte
+  // aligned pairs instead of a shift in registers. The LDS layout is that of
+  // store().
   __device__ static const float* chunk_src(const float* X, int64_t ld, int line0, int extent, int idx) {
     if constexpr (KCONTIG) {
       int line = line0 + idx / CPL;
@@ -162,15 +168,17 @@ struct Slab {
       return X + (int64_t)(idx / CPL) * ld + (col <= extent - 4 ? col : extent - 4);
     }
   }
-  __device__ static int chunk_valid(int line0, int extent, int idx) {
-    return KCONTIG ? 4 : extent - (line0 + 4 * (idx % CPL));
+  __device__ static int chunk_shift(int line0, int extent, int idx) {
+    if constexpr (KCONTIG) return 0;
+    const int valid = extent - (line0 + 4 * (idx % CPL));
+    return valid >= 1 && valid <= 3 ? 4 - valid : 0;
   }
-  __device__ static void store_chunk(float* lds, f32x4 v, int valid, int idx) {
+  __device__ static void store_chunk(float* lds, f32x4 v, int shift, int idx) {
     if constexpr (KCONTIG) {
       const int line = idx / CPL;
       *reinterpret_cast<f32x4*>(lds + line * BK + 4 * ((idx % CPL) ^ swz<BK>(line))) = v;
     } else {
-      *reinterpret_cast<f32x4*>(lds + (idx / CPL) * ROWS + 4 * (idx % CPL)) = line_end_chunk(v, valid);
+      __builtin_memcpy(lds + (idx / CPL) * ROWS + 4 * (idx % CPL) - shift, &v, sizeof(v));
     }
   }
   // Offset of the slab at k0 from the slab at k = 0.
@@ -507,7 +515,8 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
     // any other. A wave with a single 32 x 32 block keeps two accumulator
     // chains (even and odd k steps), so that no MFMA waits for the one
     // before it; they are added after the loop.
-    const bool sched = DIRECT || (nfull >= 1 && (SA::KC || M >= 4) && (SB::KC || N >= 4));
+    const bool sched = DIRECT || (nfull >= 1 && (SA::KC || (M >= 4 && (M % BM == 0 || M % BM >= 4))) &&
+                                  (SB::KC || (N >= 4 && (N % BN == 0 || N % BN >= 4))));
     if (sched) {
       static_assert(Cfg::KG == 1 && (BK / 8) % 2 == 0, "scheduled loop: no k groups, an even number of fragment sets");
       constexpr int KK = BK / 8;                 // fragment sets per slab, 8 k each
@@ -544,7 +553,7 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
 #pragma unroll
         for (int j = 0; j < FN; ++j) bf[SET][j] = SB::frag(bs, j, kk, bkey);
       };
-      // register staging: each chunk's source at k = 0 and its values inside the lines
+      // register staging: each chunk's source at k = 0 and how far before its slot it is written
       constexpr int RA = DIRECT ? 1 : SA::CHUNKS, RB = DIRECT ? 1 : SB::CHUNKS;
       const float* pa[RA];
       const float* pb[RB];
@@ -553,12 +562,12 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
 #pragma unroll
         for (int c = 0; c < RA; ++c) {
           pa[c] = SA::chunk_src(A, g.lda, m0, M, c * Cfg::NT + t);
-          va[c] = SA::chunk_valid(m0, M, c * Cfg::NT + t);
+          va[c] = SA::chunk_shift(m0, M, c * Cfg::NT + t);
         }
 #pragma unroll
         for (int c = 0; c < RB; ++c) {
           pb[c] = SB::chunk_src(B, g.ldb, n0, N, c * Cfg::NT + t);
-          vb[c] = SB::chunk_valid(n0, N, c * Cfg::NT + t);
+          vb[c] = SB::chunk_shift(n0, N, c * Cfg::NT + t);
         }
       }
       // load q of the slab at k0: a direct load into `stage`, or chunk q into registers
