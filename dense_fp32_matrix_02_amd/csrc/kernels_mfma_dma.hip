@@ -146,18 +146,15 @@ struct Slab {
     }
   }
   // Register staging without branches, for the hand-ordered loop (whole
-  // slabs; a line-contiguous operand's lines at least 4 values long, and a
-  // tile that reaches past their end holding at least 4 of them). Chunk idx
-  // of the slab at k = 0 is read from chunk_src: k-contiguous lines past the
-  // extent repeat the last line, and a line-contiguous chunk that crosses the
-  // end of the lines is read as the line's last whole chunk, which ends where
-  // the lines end. store_chunk writes it chunk_shift floats before its slot,
-  // so each value lands on its own line; the values it writes over, at the
-  // end of the previous chunk's slot, are the same ones, and the slot's own
-  // last chunk_shift floats (lines past the extent, which feed only outputs
-  // that are never stored) keep what they held. Two 64-bit writes of 4-byte
-  // aligned pairs instead of a shift in registers. The LDS layout is that of
-  // store().
+  // slabs; a line-contiguous operand's lines at least 4 values long). Chunk
+  // idx of the slab at k = 0 is read from chunk_src: k-contiguous lines past
+  // the extent repeat the last line, and a line-contiguous chunk that crosses
+  // the end of the lines is read as the line's last whole chunk, which ends
+  // where the lines end. store_chunk writes every chunk to its own slot with
+  // one 128-bit write, so in a slot whose chunk crossed the end, line c of the
+  // tile sits read_fix(c) floats after c; the fragment reads add that offset
+  // (the slot's other floats feed only outputs that are never stored). The
+  // LDS layout is otherwise that of store().
   __device__ static const float* chunk_src(const float* X, int64_t ld, int line0, int extent, int idx) {
     if constexpr (KCONTIG) {
       int line = line0 + idx / CPL;
@@ -168,17 +165,21 @@ struct Slab {
       return X + (int64_t)(idx / CPL) * ld + (col <= extent - 4 ? col : extent - 4);
     }
   }
-  __device__ static int chunk_shift(int line0, int extent, int idx) {
+  // Where line c of the tile (0 <= c < ROWS) sits in the slot chunk_src
+  // filled, relative to c: a chunk with 1 to 3 lines left before the extent
+  // was read starting 4 - valid lines early. Lines past the extent keep 0,
+  // so every read stays inside its own slot.
+  __device__ static int read_fix(int line0, int extent, int c) {
     if constexpr (KCONTIG) return 0;
-    const int valid = extent - (line0 + 4 * (idx % CPL));
-    return valid >= 1 && valid <= 3 ? 4 - valid : 0;
+    const int valid = extent - (line0 + (c & ~3));
+    return valid >= 1 && valid <= 3 && (c & 3) < valid ? 4 - valid : 0;
   }
-  __device__ static void store_chunk(float* lds, f32x4 v, int shift, int idx) {
+  __device__ static void store_chunk(float* lds, f32x4 v, int idx) {
     if constexpr (KCONTIG) {
       const int line = idx / CPL;
       *reinterpret_cast<f32x4*>(lds + line * BK + 4 * ((idx % CPL) ^ swz<BK>(line))) = v;
     } else {
-      __builtin_memcpy(lds + (idx / CPL) * ROWS + 4 * (idx % CPL) - shift, &v, sizeof(v));
+      *reinterpret_cast<f32x4*>(lds + (idx / CPL) * ROWS + 4 * (idx % CPL)) = v;
     }
   }
   // Offset of the slab at k0 from the slab at k = 0.
@@ -257,13 +258,14 @@ struct Slab {
     else return lds + 4 * h * ROWS + line_w + l32;
   }
   __device__ static int frag_key(int l32, int h) { return KCONTIG ? 4 * (h ^ swz<BK>(l32)) : 0; }
-  __device__ static f32x4 frag(const float* base, int i, int kk, int key) {
+  // fix: read_fix of the lane's line in block i, for slabs stored by store_chunk.
+  __device__ static f32x4 frag(const float* base, int i, int kk, int key, int fix = 0) {
     if constexpr (KCONTIG) {
       return *reinterpret_cast<const f32x4*>(base + 32 * i * BK + (kk ^ key));
     } else {
       f32x4 v;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = base[(kk + u) * ROWS + 32 * i];
+      for (int u = 0; u < 4; ++u) v[u] = base[(kk + u) * ROWS + 32 * i + fix];
       return v;
     }
   }
@@ -515,8 +517,7 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
     // any other. A wave with a single 32 x 32 block keeps two accumulator
     // chains (even and odd k steps), so that no MFMA waits for the one
     // before it; they are added after the loop.
-    const bool sched = DIRECT || (nfull >= 1 && (SA::KC || (M >= 4 && (M % BM == 0 || M % BM >= 4))) &&
-                                  (SB::KC || (N >= 4 && (N % BN == 0 || N % BN >= 4))));
+    const bool sched = DIRECT || (nfull >= 1 && (SA::KC || M >= 4) && (SB::KC || N >= 4));
     if (sched) {
       static_assert(Cfg::KG == 1 && (BK / 8) % 2 == 0, "scheduled loop: no k groups, an even number of fragment sets");
       constexpr int KK = BK / 8;                 // fragment sets per slab, 8 k each
@@ -543,32 +544,39 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc2[i][j][r] = 0.0f;
       }
+      // register staging: where each of this lane's fragment lines sits in its slot
+      int afix[DIRECT ? 1 : FM], bfix[DIRECT ? 1 : FN];
+      if constexpr (!DIRECT) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) afix[i] = SA::read_fix(m0, M, wm * Cfg::WTM + 32 * i + l32);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bfix[j] = SB::read_fix(n0, N, wn * Cfg::WTN + 32 * j + l32);
+      }
       f32x4 af[2][FM], bf[2][FN];
       auto read_set = [&](auto stage, auto set, int kk) __attribute__((always_inline)) {
         constexpr int SET = decltype(set)::value;
         const float* as = SA::frag_base(stage_a(stage), wm * Cfg::WTM, l32, h);
         const float* bs = SB::frag_base(stage_b(stage), wn * Cfg::WTN, l32, h);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) af[SET][i] = SA::frag(as, i, kk, akey);
+        for (int i = 0; i < FM; ++i) {
+          if constexpr (DIRECT) af[SET][i] = SA::frag(as, i, kk, akey);
+          else af[SET][i] = SA::frag(as, i, kk, akey, afix[i]);
+        }
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bf[SET][j] = SB::frag(bs, j, kk, bkey);
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (DIRECT) bf[SET][j] = SB::frag(bs, j, kk, bkey);
+          else bf[SET][j] = SB::frag(bs, j, kk, bkey, bfix[j]);
+        }
       };
-      // register staging: each chunk's source at k = 0 and how far before its slot it is written
+      // register staging: each chunk's source at k = 0
       constexpr int RA = DIRECT ? 1 : SA::CHUNKS, RB = DIRECT ? 1 : SB::CHUNKS;
       const float* pa[RA];
       const float* pb[RB];
-      int va[RA], vb[RB];
       if constexpr (!DIRECT) {
 #pragma unroll
-        for (int c = 0; c < RA; ++c) {
-          pa[c] = SA::chunk_src(A, g.lda, m0, M, c * Cfg::NT + t);
-          va[c] = SA::chunk_shift(m0, M, c * Cfg::NT + t);
-        }
+        for (int c = 0; c < RA; ++c) pa[c] = SA::chunk_src(A, g.lda, m0, M, c * Cfg::NT + t);
 #pragma unroll
-        for (int c = 0; c < RB; ++c) {
-          pb[c] = SB::chunk_src(B, g.ldb, n0, N, c * Cfg::NT + t);
-          vb[c] = SB::chunk_shift(n0, N, c * Cfg::NT + t);
-        }
+        for (int c = 0; c < RB; ++c) pb[c] = SB::chunk_src(B, g.ldb, n0, N, c * Cfg::NT + t);
       }
       // load q of the slab at k0: a direct load into `stage`, or chunk q into registers
       auto load_one = [&](int q, int k0, auto stage) __attribute__((always_inline)) {
@@ -587,9 +595,9 @@ __global__ void __launch_bounds__(Cfg::NT, DIRECT ? Cfg::WAVES_EU : 1) mfma_dma_
       // register chunk q to `stage`
       auto store_one = [&](int q, auto stage) __attribute__((always_inline)) {
         if (q < NA)
-          SA::store_chunk(stage_a(stage), ra[q], va[q], q * Cfg::NT + t);
+          SA::store_chunk(stage_a(stage), ra[q], q * Cfg::NT + t);
         else
-          SB::store_chunk(stage_b(stage), rb[q - NA], vb[q - NA], (q - NA) * Cfg::NT + t);
+          SB::store_chunk(stage_b(stage), rb[q - NA], (q - NA) * Cfg::NT + t);
       };
       using Z = std::integral_constant<int, 0>;
       auto group = [&](auto cur, auto gi_c, int k1) __attribute__((always_inline)) {

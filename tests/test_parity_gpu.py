@@ -405,21 +405,24 @@ def test_direct_lds_configs_exact(cid):
     np.testing.assert_array_equal(Cs.cpu().numpy(), oracle.sgemm_f32(np_(A), np_(B)))
 
 
-RS_IDS = [i for i, n in enumerate(CONFIG_NAMES) if re.search(r"_rs\d*_sched", n)]
+# the register-staged configurations, and the direct ones, whose misaligned
+# operands run the same hand-ordered loop staged through registers
+SCHED_IDS = [i for i, n in enumerate(CONFIG_NAMES) if n.endswith("_sched") or "_sched_" in n]
 
 
-@pytest.mark.parametrize("cid", RS_IDS, ids=[CONFIG_NAMES[i] for i in RS_IDS])
+@pytest.mark.parametrize("cid", SCHED_IDS, ids=[CONFIG_NAMES[i] for i in SCHED_IDS])
 def test_register_staged_hand_ordered_any_alignment(cid):
     """The hand-ordered loop staged through registers takes bases at any
     4-byte offset, odd leading dimensions and extents that are not multiples
     of 4, in the operand layouts the configuration reads: lines past the edge
     of C repeat the last line, a chunk that crosses the end of a
     line-contiguous operand's lines is read as the line's last whole chunk and
-    moved into place, a K that is not a whole number of slabs ends in a slab
-    staged on its own, and problems under one slab deep, or with fewer than 4
-    lines where the lines are contiguous, take the plain register loop. Exact
-    on integer inputs, with NaN around every operand and in C's padding,
-    which must stay."""
+    its lines are found at an offset in their slot (also where the last tile
+    holds only 1 to 3 of them), a K that is not a whole number of slabs ends
+    in a slab staged on its own, and problems under one slab deep, or with
+    fewer than 4 lines where the lines are contiguous, take the plain register
+    loop. Exact on integer inputs, with NaN around every operand and in C's
+    padding, which must stay."""
     bm, bn, bk, _ = sg.sgemm_mi355_config_info(cid)
     opA, opB = sg.sgemm_mi355_config_ops(cid)
     cases = [  # M, N, K, lda pad, ldb pad, ldc pad, A offset, B offset, C offset (floats)
@@ -429,6 +432,8 @@ def test_register_staged_hand_ordered_any_alignment(cid):
         (3, bn + 1, 5 * bk + 1, 2, 1, 2, 2, 3, 0),
         (bm - 1, 2, 2 * bk + 31, 1, 0, 1, 0, 1, 2),
         (bm + 7, 5, 3 * bk, 3, 2, 0, 1, 3, 1),
+        (bm + 2, bn + 2, 3 * bk + 5, 1, 1, 0, 2, 1, 0),  # 2 lines in the last tile of each
+        (2 * bm + 3, 2 * bn + 3, 2 * bk, 0, 2, 1, 1, 0, 2),  # 3 lines in the last tile of each
         (2 * bm, 2 * bn, bk - 1, 1, 1, 1, 2, 1, 3),
         (3001 % bm + bm, 2047 % bn + bn, 1537, 0, 0, 0, 0, 0, 0),
     ]
